@@ -1,0 +1,309 @@
+"""Float64 host implementations of attention and of the pages' softmax recurrences.
+
+Test infrastructure only (see the package docstring): nothing on the product
+path may import this module.
+
+``attention`` is the oracle proper.  The pages state that the tiled one-pass
+method reaches exactly the result of standard attention ("identical" /
+"exactly the same" in the quidproquo.cc guide's TL;DR and "The scene"
+section; "mathematically equivalent" in the comfyai.app chapter's
+introduction), so the oracle is that plain definition written out: it
+materialises every score, subtracts the row maximum, exponentiates, sums,
+divides and only then takes the weighted sum of the values.
+
+The other functions are independent evaluations of the same quantities that
+follow the pages' recurrences step by step.  They exist to pin ``attention``
+and each other in the CPU test tier; none of them shares arithmetic with the
+GPU kernels.
+
+Conventions (readings of points the pages leave open):
+
+* scores are ``a_ij = scale * (q_i . k_j)``; the guide writes the plain dot
+  product (slides 3-4) and the comfyai chapter names a "scale" step of the
+  fused tile without a surviving formula;
+* causal masking is aligned to the bottom-right corner: query ``i`` of ``Lq``
+  may see key ``j`` of ``Lk`` iff ``j <= i + (Lk - Lq)``; masked scores are
+  minus infinity, so they drop out of both the maximum and the sum;
+* the log-sum-exp returned per row is ``m + ln(s)`` in natural-log units of
+  the scaled scores, where ``m`` is the row maximum and ``s`` the
+  denominator.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence
+
+import numpy as np
+
+__all__ = [
+    "attention",
+    "two_pass_chunked",
+    "one_pass_chunked",
+    "decoupled_softmax",
+    "tiled_outer_kv",
+]
+
+
+def _allowed_keys(rows: np.ndarray, Lq: int, Lk: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), Lk] mask of the keys each query row may attend to."""
+    j = np.arange(Lk)[None, :]
+    if not causal:
+        return np.ones((rows.shape[0], Lk), dtype=bool)
+    return j <= (rows[:, None] + (Lk - Lq))
+
+
+def attention(q, k, v, scale: float, causal: bool = False, rows=None,
+              row_block: int = 1024, check: bool = True):
+    """Exact attention forward, materialised, in float64.
+
+    Follows standard attention as both pages describe it: the guide's
+    self-attention review (slides 3-4: dot products ``a_i``, softmax to
+    ``a^_i``, weighted sum of ``v_i``) with the "subtract Amax before taking
+    the exponential" step of its naive multi-pass walk-through (slides 11-17),
+    which the comfyai chapter calls safe softmax (section 6.3.2).
+
+    Args:
+      q: [B, H, Lq, D] array of any real float dtype (upcast exactly).
+      k, v: [B, H, Lk, D].
+      scale: multiplier applied to every dot product before the softmax.
+      causal: bottom-right aligned causal mask (requires Lq <= Lk).
+      rows: optional 1-D integer array of query rows to evaluate; the result
+        then has ``len(rows)`` rows in that order.
+      row_block: rows per materialised score block (bounds host memory).
+      check: run the internal consistency checks listed below.
+
+    Returns:
+      (O, LSE): O is [B, H, R, D] float64 and LSE is [B, H, R] float64,
+      with R = Lq or len(rows).
+
+    Internal checks (``check=True``): every weight row sums to one within
+    1e-13; ``m <= LSE <= m + ln(#allowed keys)``; each output element lies in
+    the range of the value column it averages (a convex combination).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+        raise ValueError("k and v must be [B, H, Lk, D] matching q")
+    if causal and Lq > Lk:
+        raise ValueError("causal attention needs Lq <= Lk")
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    O = np.zeros((B, H, R, D), dtype=np.float64)
+    LSE = np.zeros((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kk = k[b, h].astype(np.float64)
+            vv = v[b, h].astype(np.float64)
+            for r0 in range(0, R, row_block):
+                rr = rows[r0:r0 + row_block]
+                qq = q[b, h, rr].astype(np.float64)
+                # Scores a_ij = scale * q_i . k_j for every key.
+                a = scale * (qq @ kk.T)
+                allowed = _allowed_keys(rr, Lq, Lk, causal)
+                a = np.where(allowed, a, -np.inf)
+                # Pass 1: the row maximum Amax.
+                m = a.max(axis=1)
+                # Pass 2: exp(a_i - Amax) (masked entries become exactly 0).
+                e = np.exp(a - m[:, None])
+                # Pass 3: the denominator.
+                s = e.sum(axis=1)
+                # Pass 4: the weights a^_i.
+                p = e / s[:, None]
+                # Pass 5: the weighted sum of the values.
+                o = p @ vv
+                O[b, h, r0:r0 + len(rr)] = o
+                LSE[b, h, r0:r0 + len(rr)] = m + np.log(s)
+                if check:
+                    _check_block(p, o, m, m + np.log(s), allowed, vv)
+    return O, LSE
+
+
+def _check_block(p, o, m, lse, allowed, vv):
+    n_allowed = allowed.sum(axis=1)
+    if np.max(np.abs(p.sum(axis=1) - 1.0)) > 1e-13:
+        raise AssertionError("oracle: weight rows do not sum to one")
+    tol = 1e-12 * np.maximum(1.0, np.abs(m))
+    if np.any(lse < m - tol) or np.any(lse > m + np.log(n_allowed) + tol):
+        raise AssertionError("oracle: LSE outside [m, m + ln(#keys)]")
+    # Convex combination: O[i, d] lies within the range of v[:, d] over the
+    # keys row i may see.  Small blocks check per row; large blocks check
+    # against the range over all keys (cheaper, still a valid bound).
+    if o.shape[0] * vv.shape[0] <= (1 << 16):
+        sel = allowed[:, :, None]
+        lo = np.where(sel, vv[None, :, :], np.inf).min(axis=1)
+        hi = np.where(sel, vv[None, :, :], -np.inf).max(axis=1)
+    else:
+        lo = vv.min(axis=0)[None, :]
+        hi = vv.max(axis=0)[None, :]
+    slack = 1e-12 * np.maximum(1.0, np.abs(lo) + np.abs(hi))
+    if np.any(o < lo - slack) or np.any(o > hi + slack):
+        raise AssertionError("oracle: output outside the range of V")
+
+
+def _chunks(n: int, bounds: Sequence[int]) -> Iterable[slice]:
+    """Slices for chunk boundaries ``0 = b0 < b1 < ... < bK = n``."""
+    b = list(bounds)
+    if b[0] != 0 or b[-1] != n or any(x >= y for x, y in zip(b, b[1:])):
+        raise ValueError("bounds must increase strictly from 0 to n")
+    for x, y in zip(b, b[1:]):
+        yield slice(x, y)
+
+
+def two_pass_chunked(a, bounds):
+    """Softmax of one score row in two reads, chunk by chunk.
+
+    The guide's simplified mechanism (slides 18-24): the first read keeps a
+    running maximum ``d_k`` and a running denominator ``s_k``, with
+    ``d_k = max(d_{k-1}, max of chunk k)`` and
+    ``s_k = s_{k-1} exp(d_{k-1} - d_k) + sum_{i in chunk k} exp(a_i - d_k)``;
+    the second read forms ``a^_i = exp(a_i - d_B) / s_B``.
+
+    A chunk whose scores are all minus infinity (fully masked) contributes
+    nothing and is skipped while no finite maximum exists yet, so that
+    ``(-inf) - (-inf)`` never occurs.
+
+    Returns (weights, d_B, s_B).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    d = -math.inf
+    s = 0.0
+    for c in _chunks(a.shape[0], bounds):
+        chunk_max = float(np.max(a[c]))
+        d_new = max(d, chunk_max)
+        if d_new == -math.inf:
+            continue
+        rescale = math.exp(d - d_new) if d != -math.inf else 0.0
+        s = s * rescale + float(np.sum(np.exp(a[c] - d_new)))
+        d = d_new
+    w = np.exp(a - d) / s
+    return w, d, s
+
+
+def one_pass_chunked(a, vals, bounds):
+    """Weighted sum of value rows in one read, with the output correction.
+
+    The guide's full mechanism (slides 25-27): after each chunk ``k`` the
+    running output is normalised with the chunk's ``d_k`` and ``s_k``:
+    ``O_k = O_{k-1} (s_{k-1} / s_k) exp(d_{k-1} - d_k)
+            + sum_{i in chunk k} exp(a_i - d_k) / s_k * v_i``,
+    starting from ``O_0 = 0``, ``s_0 = 0``, ``d_0 = -inf``; after the last
+    chunk ``O_B = sum_i a^_i v_i``.
+
+    Args:
+      a: [L] scores.
+      vals: [L, Dv] value rows.
+      bounds: chunk boundaries from 0 to L.
+
+    Returns (O_B, d_B, s_B).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    vals = np.asarray(vals, dtype=np.float64)
+    if vals.ndim == 1:
+        vals = vals[:, None]
+    O = np.zeros(vals.shape[1], dtype=np.float64)
+    d = -math.inf
+    s = 0.0
+    for c in _chunks(a.shape[0], bounds):
+        d_new = max(d, float(np.max(a[c])))
+        if d_new == -math.inf:
+            continue
+        e = np.exp(a[c] - d_new)
+        first = d == -math.inf
+        s_new = (0.0 if first else s * math.exp(d - d_new)) + float(e.sum())
+        carried = np.zeros_like(O) if first else O * (s / s_new) * math.exp(d - d_new)
+        O = carried + (e / s_new) @ vals[c]
+        d, s = d_new, s_new
+    return O, d, s
+
+
+def decoupled_softmax(x, bounds):
+    """Softmax over blocks with per-block statistics, merged afterwards.
+
+    The comfyai chapter's "Decoupled Softmax" and its "A Simple Example"
+    (section 6.3.3): each block ``j`` keeps its own maximum ``m~_j`` and sum
+    ``l~_j = sum exp(x - m~_j)``; blocks merge by
+    ``m_new = max(m, m~_j)`` and
+    ``l_new = exp(m - m_new) l + exp(m~_j - m_new) l~_j``,
+    and each block's numerators are rescaled by ``exp(m~_j - m_final)``.
+
+    Returns (softmax, m_final, l_final, per_block) where ``per_block`` lists
+    (m~_j, l~_j) in block order.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = -math.inf
+    l = 0.0
+    per_block = []
+    for c in _chunks(x.shape[0], bounds):
+        m_blk = float(np.max(x[c]))
+        l_blk = float(np.sum(np.exp(x[c] - m_blk)))
+        per_block.append((m_blk, l_blk))
+        m_new = max(m, m_blk)
+        l = (math.exp(m - m_new) * l if m != -math.inf else 0.0) + math.exp(m_blk - m_new) * l_blk
+        m = m_new
+    out = np.empty_like(x)
+    for c, (m_blk, _) in zip(_chunks(x.shape[0], bounds), per_block):
+        out[c] = np.exp(x[c] - m_blk) * math.exp(m_blk - m) / l
+    return out, m, l, per_block
+
+
+def tiled_outer_kv(q, k, v, scale: float, causal: bool = False,
+                   block_r: int = 4, block_c: int = 4):
+    """One head of attention in the comfyai chapter's tile order.
+
+    Follows the "Full Forward Process" of section 6.3.3: O, l and m are
+    initialised (to 0, 0 and minus infinity) in "HBM" (here host arrays);
+    the outer loop walks the key/value blocks K_j, V_j of ``block_c`` rows;
+    the inner loop walks the query blocks Q_i of ``block_r`` rows, reads back
+    O_i, l_i, m_i, computes the block scores S_ij = scale Q_i K_j^T, the
+    block statistics m~_ij (row max), P~_ij = exp(S_ij - m~_ij) and
+    l~_ij (row sum), merges them into m_new = max(m_i, m~_ij) and
+    l_new = exp(m_i - m_new) l_i + exp(m~_ij - m_new) l~_ij, updates
+    O_i <- (l_i exp(m_i - m_new) O_i + exp(m~_ij - m_new) P~_ij V_j) / l_new
+    and writes O_i, l_i, m_i back.
+
+    Rows of a block with no allowed key in K_j (causal) keep their state.
+
+    Args:
+      q: [Lq, D]; k, v: [Lk, D].
+
+    Returns (O [Lq, D], LSE [Lq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Lq, Lk = q.shape[0], k.shape[0]
+    O = np.zeros((Lq, v.shape[1]))
+    l = np.zeros(Lq)
+    m = np.full(Lq, -np.inf)
+    for j0 in range(0, Lk, block_c):
+        Kj = k[j0:j0 + block_c]
+        Vj = v[j0:j0 + block_c]
+        cols = np.arange(j0, j0 + Kj.shape[0])
+        for i0 in range(0, Lq, block_r):
+            rows = np.arange(i0, min(i0 + block_r, Lq))
+            S = scale * (q[rows] @ Kj.T)
+            if causal:
+                S = np.where(cols[None, :] <= rows[:, None] + (Lk - Lq), S, -np.inf)
+            live = np.isfinite(S).any(axis=1)
+            if not live.any():
+                continue
+            r = rows[live]
+            S = S[live]
+            m_t = S.max(axis=1)
+            P_t = np.exp(S - m_t[:, None])
+            l_t = P_t.sum(axis=1)
+            m_old = m[r]
+            m_new = np.maximum(m_old, m_t)
+            a_old = np.where(np.isfinite(m_old), np.exp(m_old - m_new), 0.0)
+            a_new = np.exp(m_t - m_new)
+            l_new = a_old * l[r] + a_new * l_t
+            O[r] = ((l[r] * a_old)[:, None] * O[r] + a_new[:, None] * (P_t @ Vj)) / l_new[:, None]
+            l[r] = l_new
+            m[r] = m_new
+    return O, m + np.log(l)
