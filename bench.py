@@ -1,0 +1,224 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic
+input: the causal bf16 prefill (B=1, H=32, L=8192, D=128, x8 queries on
+heads 0-3) followed by the split-KV bf16 decode (B=16, H=32, Lk=32768,
+D=128).  Inputs are resident in device memory before timing starts.  W
+untimed warm-up steps, then exactly K timed steps bracketed by device
+synchronisation; each kernel call is also bracketed by HIP events on the
+stream it runs on, which gives the per-launch durations behind the roofline
+figures.
+
+Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
+(4 B H Lq Lk D flops, halved for causal, over the prefill's own average
+duration); the decode throughput (K+V bytes over the decode call's average
+duration) is reported under ``decode``.  ``cpu_baseline`` times the float64
+CPU oracle on a bounded sample of the prefill workload (test infrastructure,
+never part of the timed path).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+PREFILL = "causal_bf16_8k"
+DECODE = "decode_bf16_32k"
+
+
+def _parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--splits", type=int, default=0, help="decode split count (0 = library choice)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=24, help="heads of the prefill workload the oracle times")
+    return p.parse_args()
+
+
+def _traffic(kernel_file: str, summary: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = ROOT / "profiles" / summary
+    src = ROOT / "io_aware_softmax_amd" / "csrc" / kernel_file
+    if not path.exists():
+        return None
+    fields = {}
+    for line in path.read_text().splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != hashlib.sha256(src.read_bytes()).hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _to_device(bits, dtype):
+    import numpy as np
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(bits).cuda()
+    t = torch.from_numpy(bits.view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def _cpu_baseline(wl, heads: int):
+    """Time the float64 oracle on the first ``heads`` heads (all rows)."""
+    import numpy as np
+    import oracle
+    from io_aware_softmax_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    slabs = [{t: inputs.slab_values(wl, t, 0, h)[None, None] for t in "qkv"} for h in range(heads)]
+    t0 = time.perf_counter()
+    for s in slabs:
+        oracle.attention(s["q"], s["k"], s["v"], wl.scale, wl.causal)
+    dt = time.perf_counter() - t0
+    flops = wl.flops() * heads / (wl.B * wl.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"heads 0-{heads - 1} of {wl.H} (all {wl.Lq} rows) of the causal bf16 prefill, "
+                      f"float64 NumPy, {dt:.1f} s for {flops:.3e} algorithmic flops"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from io_aware_softmax_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+
+    wp = inputs.WORKLOADS[PREFILL]
+    wd = inputs.WORKLOADS[DECODE]
+    run_p = run_d = True
+
+    t_gen = time.perf_counter()
+    if run_p:
+        bp = inputs.generate(wp)
+        qp, kp, vp = (_to_device(bp[t], wp.dtype) for t in "qkv")
+        del bp
+        op = torch.empty_like(qp)
+        lp = torch.empty(wp.B, wp.H, wp.Lq, dtype=torch.float32, device="cuda")
+    if run_d:
+        bd = inputs.generate(wd)
+        qd, kd, vd = (_to_device(bd[t], wd.dtype) for t in "qkv")
+        del bd
+        od = torch.empty_like(qd)
+        ld = torch.empty(wd.B, wd.H, 1, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+    splits = args.splits or binding.attn_decode_auto_splits(wd.B, wd.H, wd.Lk, wd.D)
+
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if run_p:
+            if evs is not None:
+                evs[0].record(stream)
+            binding.attn_fwd(qp, kp, vp, causal=wp.causal, scale=wp.scale, out=op, lse=lp)
+            if evs is not None:
+                evs[1].record(stream)
+        if run_d:
+            if evs is not None:
+                evs[2].record(stream)
+            binding.attn_decode_fwd(qd, kd, vd, scale=wd.scale, num_splits=splits, out=od, lse=ld)
+            if evs is not None:
+                evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    p_ms = [e[0].elapsed_time(e[1]) for e in evs] if run_p else [0.0]
+    d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [0.0]
+    p_avg = float(np.mean(p_ms))
+    d_avg = float(np.mean(d_ms))
+    ms_per_step = wall * 1e3 / args.steps
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (causal bf16 prefill B1 H32 L8192 D128)",
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal bf16 prefill B1 H32 Lq=Lk=8192 D128 (q x8 on heads 0-3) "
+                        "+ split-KV bf16 decode B16 H32 Lk32768 D128",
+            "prefill": {"B": wp.B, "H": wp.H, "Lq": wp.Lq, "Lk": wp.Lk, "D": wp.D, "causal": True,
+                        "scale": wp.scale, "flops": wp.flops()},
+            "decode": {"B": wd.B, "H": wd.H, "Lq": 1, "Lk": wd.Lk, "D": wd.D, "splits": splits,
+                       "kv_bytes": wd.kv_bytes()},
+            "parallelism": "single GPU",
+        },
+    }
+    if run_p:
+        tflops = wp.flops() / (p_avg * 1e-3) / 1e12
+        rec["value"] = tflops
+        rec["ms_prefill"] = p_avg
+        rec["ms_prefill_min"] = float(np.min(p_ms))
+        rec["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                           "traffic": _traffic("prefill_mfma.hip", "prefill_causal_bf16_8k_traffic.txt"),
+                           "kernel": "prefill_mfma_kernel<bf16, D=128, causal>"}
+    if run_d:
+        gbs = wd.kv_bytes() / (d_avg * 1e-3) / 1e9
+        rec["decode"] = {"metric": "decode HBM GB/s (K+V bytes / decode call time)", "value": gbs,
+                         "unit": "GB/s", "ms": d_avg, "ms_min": float(np.min(d_ms)),
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": _traffic("decode.hip", "decode_bf16_32k_traffic.txt"),
+                                      "kernel": "decode_split_kernel<bf16, D=128> + decode_combine_kernel"}}
+    rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                     "arch": getattr(props, "gcnArchName", "")}
+    rec["input_gen_s"] = gen_s
+    if run_p and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _cpu_baseline(wp, args.cpu_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * attn.h - C ABI of the exact attention forward for AMD MI355X (gfx950).
+ *
+ * The library computes O = softmax(scale * Q K^T) V for every (batch, head)
+ * in one pass over key/value tiles, keeping a running row maximum, a running
+ * denominator and a rescaled output accumulator on chip, and never writing
+ * the L x L weights to device memory.  The recurrence is the one the
+ * quidproquo.cc guide "NTU Hung-yi Lee ML 2026 Guide: Faster Generation,
+ * Part 1: Flash Attention" derives in "Mechanism: run with the wrong answer,
+ * then correct it" (its two "Expand" boxes: the running maximum d_k, the
+ * running denominator s_k, and the output correction by
+ * (s_{k-1}/s_k) exp(d_{k-1} - d_k)); the tiled, fused form is the one the
+ * comfyai.app chapter "6.3 FlashAttention" (section 6.3.3) describes.  The
+ * result equals standard attention up to floating-point rounding.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major
+ *     tensors: q and o are [B, H, Lq, D], k and v are [B, H, Lk, D], lse is
+ *     [B, H, Lq] float32.  q, k, v and o share `dtype`.  There are no
+ *     strides.  Every tensor pointer must be 16-byte aligned.
+ *   - scores are a_ij = scale * (q_i . k_j); any finite scale is accepted.
+ *   - causal != 0 applies a bottom-right aligned mask: query i may attend to
+ *     key j iff j <= i + (Lk - Lq).  Causal requires Lq <= Lk.
+ *   - lse[i] = m_i + ln(sum_j exp(a_ij - m_i)) with m_i the row maximum, in
+ *     natural-log units of the scaled scores.
+ *   - o is written in `dtype` (round to nearest even from float32); lse in
+ *     float32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous: it validates, enqueues kernels on `stream` and returns.
+ *     Inputs must stay valid and unmodified until the stream reaches the
+ *     work; o and lse are complete when the stream has passed it.
+ *   - Ownership: the caller owns every buffer; the library frees nothing it
+ *     did not allocate.  o and lse must not overlap q, k, v or each other.
+ *     The library keeps no state between calls and may be called from
+ *     several host threads.
+ *   - Errors: a negative attn_status_t.  All argument checks run before any
+ *     HIP call, so a rejected call has no effect.  ATTN_ERR_HIP reports a
+ *     failed launch or allocation; faults inside a kernel surface later, at
+ *     the caller's stream synchronisation.  NaN or Inf in the inputs is not
+ *     checked and propagates.
+ */
+#ifndef IO_AWARE_SOFTMAX_ATTN_H
+#define IO_AWARE_SOFTMAX_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,  /* IEEE binary32 */
+  ATTN_F16 = 1,  /* IEEE binary16 */
+  ATTN_BF16 = 2  /* bfloat16 */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,           /* a required pointer is NULL */
+  ATTN_ERR_DIM = -2,            /* a dimension <= 0, or a size that overflows the index types */
+  ATTN_ERR_UNSUPPORTED_D = -3,  /* head dim D is not 64 or 128 */
+  ATTN_ERR_DTYPE = -4,          /* unknown attn_dtype_t */
+  ATTN_ERR_SCALE = -5,          /* scale is NaN or infinite */
+  ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal with Lq > Lk */
+  ATTN_ERR_SPLITS = -7,         /* num_splits outside [0, ATTN_MAX_SPLITS] */
+  ATTN_ERR_ALIAS = -8,          /* o or lse overlaps an input or each other */
+  ATTN_ERR_ALIGN = -9,          /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_HIP = -10            /* a HIP launch or allocation failed */
+} attn_status_t;
+
+/* Largest split count accepted by attn_decode_fwd. */
+#define ATTN_MAX_SPLITS 256
+
+/*
+ * attn_fwd - attention forward for any supported shape.
+ *
+ * q [B,H,Lq,D], k [B,H,Lk,D], v [B,H,Lk,D], o [B,H,Lq,D] (all `dtype`),
+ * lse [B,H,Lq] float32.  D must be 64 or 128.
+ *
+ * Lq == 1 runs the split-KV decode path with the split count chosen by the
+ * library (causal is then the same as non-causal); any other Lq runs the
+ * tiled prefill kernel (MFMA for every dtype).  The decode path allocates a
+ * stream-ordered workspace of (D + 2) * 4 * B * H * splits bytes with
+ * hipMallocAsync on `stream` and releases it on the same stream.
+ *
+ * Returns ATTN_OK or a negative attn_status_t.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Lq, int Lk, int D, int causal, float scale,
+             void* stream, int dtype);
+
+/*
+ * attn_decode_fwd - single-query (Lq = 1) attention by split-KV.
+ *
+ * q and o are [B,H,1,D]; k and v are [B,H,Lk,D]; lse is [B,H,1].  The Lk
+ * keys of each (b, h) are cut into `num_splits` contiguous ranges of
+ * ceil(Lk / num_splits) keys (the last ones may be short or empty).  One
+ * kernel computes, per range p, the partial statistics d_p (maximum),
+ * s_p (denominator) and the normalised partial output O_p; a second kernel
+ * merges them with the guide's output correction, treating each range as
+ * one chunk: d = max_p d_p, s = sum_p s_p exp(d_p - d),
+ * O = sum_p O_p (s_p / s) exp(d_p - d).  Empty ranges are skipped.
+ *
+ * num_splits == 0 lets the library choose.  Workspace as for attn_fwd.
+ */
+int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Lk, int D, float scale, int num_splits,
+                    void* stream, int dtype);
+
+/*
+ * attn_decode_auto_splits - the split count attn_fwd and attn_decode_fwd
+ * (with num_splits == 0) use for this shape.  Pure host arithmetic; returns
+ * a value in [1, ATTN_MAX_SPLITS], or a negative attn_status_t for invalid
+ * dimensions.
+ */
+int attn_decode_auto_splits(int B, int H, int Lk, int D);
+
+/*
+ * attn_strerror - static description of a status code.  For ATTN_ERR_HIP
+ * the text of the last HIP error seen by the calling host thread is
+ * appended; the returned pointer stays valid until that thread's next
+ * library call.
+ */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_SOFTMAX_ATTN_H */

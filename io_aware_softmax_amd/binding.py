@@ -1,0 +1,164 @@
+"""ctypes binding of libattn.so with the C ABI's names (argument marshalling only).
+
+Every computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and the current HIP stream; nothing here computes attention, and there
+is no fallback: if the library is missing, every call raises
+``AttnLibraryMissing``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from pathlib import Path
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_MAX_SPLITS = 256
+_DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_auto_splits", "attn_strerror")
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+
+class AttnLibraryMissing(RuntimeError):
+    """libattn.so has not been built (run ``__graft_entry__.build()``)."""
+
+
+class AttnError(RuntimeError):
+    """A negative status from the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn status {status}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so once and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not LIB_PATH.exists():
+            raise AttnLibraryMissing(
+                f"{LIB_PATH} not found; build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
+        lib.attn_fwd.restype = i
+        lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
+        lib.attn_decode_fwd.restype = i
+        lib.attn_decode_auto_splits.argtypes = [i, i, i, i]
+        lib.attn_decode_auto_splits.restype = i
+        lib.attn_strerror.argtypes = [i]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def attn_strerror(status: int) -> str:
+    return load().attn_strerror(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, attn_strerror(status))
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _prep(q, k, v, out, lse, Lq):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, L, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one of float32, float16, bfloat16")
+    B, H, _, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if not out.is_contiguous() or not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("out and lse must be contiguous (lse float32)")
+    return out, lse
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, LSE = attention(q, k, v) through ``attn_fwd`` of the C ABI.
+
+    q [B,H,Lq,D], k and v [B,H,Lk,D], contiguous, on the GPU.  Returns the
+    output [B,H,Lq,D] (dtype of q) and the log-sum-exp [B,H,Lq] (float32).
+    ``scale`` defaults to 1/sqrt(D).  Asynchronous on ``stream`` (default:
+    torch's current stream).
+    """
+    lib = load()
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    out, lse = _prep(q, k, v, out, lse, Lq)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Lq, Lk, D, int(bool(causal)), scale, _stream_handle(stream),
+                        _DTYPE_CODES[q.dtype]))
+    return out, lse
+
+
+def attn_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                    num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV single-query attention through ``attn_decode_fwd``.
+
+    q [B,H,1,D]; ``num_splits`` 0 lets the library choose.
+    """
+    lib = load()
+    B, H, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("attn_decode_fwd takes one query per (batch, head)")
+    Lk = k.shape[2]
+    out, lse = _prep(q, k, v, out, lse, 1)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_decode_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, Lk, D, scale, int(num_splits),
+                               _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return out, lse
+
+
+def attn_decode_auto_splits(B: int, H: int, Lk: int, D: int) -> int:
+    s = load().attn_decode_auto_splits(B, H, Lk, D)
+    _check(min(s, 0))
+    return s
+
+
+def raw_attn_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                 Lq: int, Lk: int, D: int, causal: int, scale: float, stream: int, dtype: int) -> int:
+    """The C entry point with plain integers for pointers; returns the status."""
+    return load().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Lq, Lk, D, causal, scale,
+                           stream, dtype)
+
+
+def raw_attn_decode_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                        Lk: int, D: int, scale: float, num_splits: int, stream: int, dtype: int) -> int:
+    return load().attn_decode_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Lk, D, scale, num_splits,
+                                  stream, dtype)
+
+
+def library_loaded_path() -> str:
+    """Absolute path of the loaded library (for provenance checks)."""
+    load()
+    return os.fspath(LIB_PATH)

@@ -1,0 +1,165 @@
+// C ABI of the attention forward: argument validation, kernel dispatch and
+// the decode workspace.  Declarations and the contract are in include/attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "attn_internal.hpp"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_hip_msg[192] = "";
+thread_local char g_status_msg[256] = "";
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_hip_msg, sizeof(g_hip_msg), "%s (%s)", hipGetErrorString(e), hipGetErrorName(e));
+  return ATTN_ERR_HIP;
+}
+
+size_t elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Launch-size limit: grid size times block size must fit 32 bits.
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 24) - 1;
+
+// Everything that does not need the device; returns ATTN_OK or an error.
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+             int H, int Lq, int Lk, int D, int causal, float scale, int dtype) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return ATTN_ERR_DIM;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+  const int64_t BH = int64_t(B) * H;
+  if (BH > INT32_MAX || int64_t(Lq) * D > INT32_MAX || int64_t(Lk) * D > INT32_MAX)
+    return ATTN_ERR_DIM;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (causal && Lq > Lk) return ATTN_ERR_CAUSAL_SHAPE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+  if ((mis & 15u) || (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
+  const size_t es = elem_bytes(dtype);
+  const size_t nq = size_t(BH) * Lq * D * es, nk = size_t(BH) * Lk * D * es;
+  const size_t nl = size_t(BH) * Lq * sizeof(float);
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
+      overlaps(o, nq, lse, nl))
+    return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+int auto_splits(int64_t BH, int Lk) {
+  // Aim for about 16 workgroups per CU of the 256-CU part, but keep at least
+  // 256 keys per range so the per-range epilogue stays negligible.
+  const int64_t target = 4096;
+  int64_t s = (target + BH - 1) / BH;
+  const int64_t by_len = (int64_t(Lk) + 255) / 256;
+  if (s > by_len) s = by_len;
+  if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return int(s);
+}
+
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Lk, int D, float scale, int splits, hipStream_t stream, int dtype) {
+  const int64_t BH = int64_t(B) * H;
+  if (splits == 0) splits = auto_splits(BH, Lk);
+  if (BH * splits > kMaxWorkgroups) return ATTN_ERR_DIM;
+  const size_t nparts = size_t(BH) * splits;
+  const size_t bytes = nparts * (size_t(D) + 2) * sizeof(float);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(ws);
+  a.part_m = a.part_o + nparts * D;
+  a.part_l = a.part_m + nparts;
+  a.BH = int(BH);
+  a.Lk = Lk;
+  a.splits = splits;
+  a.keys_per_split = int((int64_t(Lk) + splits - 1) / splits);
+  a.c = std::fabs(scale) * attn::kLog2e;
+  a.neg = scale < 0.f;
+  e = attn::launch_decode(dtype, D, a, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Lq, int Lk, int D, int causal, float scale, void* stream,
+                         int dtype) {
+  const int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Lq == 1) return run_decode(q, k, v, o, lse, B, H, Lk, D, scale, 0, s, dtype);
+  attn::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.c = std::fabs(scale) * attn::kLog2e;
+  a.neg = scale < 0.f;
+  const int64_t nqt = (int64_t(Lq) + 127) / 128;
+  if (int64_t(a.BH) * nqt > kMaxWorkgroups) return ATTN_ERR_DIM;
+  const hipError_t e = dtype == ATTN_F32 ? attn::launch_prefill_f32(D, causal != 0, a, s)
+                                         : attn::launch_prefill_mfma(dtype, D, causal != 0, a, s);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+ATTN_EXPORT int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Lk, int D, float scale, int num_splits,
+                                void* stream, int dtype) {
+  const int st = validate(q, k, v, o, lse, B, H, 1, Lk, D, 0, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  return run_decode(q, k, v, o, lse, B, H, Lk, D, scale, num_splits, static_cast<hipStream_t>(stream),
+                    dtype);
+}
+
+ATTN_EXPORT int attn_decode_auto_splits(int B, int H, int Lk, int D) {
+  if (B <= 0 || H <= 0 || Lk <= 0 || D <= 0) return ATTN_ERR_DIM;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
+  if (int64_t(B) * H > INT32_MAX) return ATTN_ERR_DIM;
+  return auto_splits(int64_t(B) * H, Lk);
+}
+
+ATTN_EXPORT const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_DIM: return "a dimension is <= 0 or a size exceeds the index range";
+    case ATTN_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
+    case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_F32, ATTN_F16 or ATTN_BF16)";
+    case ATTN_ERR_SCALE: return "scale is NaN or infinite";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires Lq <= Lk";
+    case ATTN_ERR_SPLITS: return "num_splits must be in [0, ATTN_MAX_SPLITS]";
+    case ATTN_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_HIP:
+      std::snprintf(g_status_msg, sizeof(g_status_msg), "HIP error: %s", g_hip_msg);
+      return g_status_msg;
+    default: return "unknown status";
+  }
+}

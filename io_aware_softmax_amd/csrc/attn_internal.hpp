@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace attn {
+
+// log2(e): scores are moved to base 2 so that exp becomes one v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;        // B * H
+  int Lq;
+  int Lk;
+  float c;       // |scale| * log2(e)
+  bool neg;      // scale < 0: q is negated on load (exact)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* part_o;  // [BH, splits, D] normalised partial outputs
+  float* part_m;  // [BH, splits] partial maxima, base-2 scaled-score units
+  float* part_l;  // [BH, splits] partial denominators
+  int BH;
+  int Lk;
+  int splits;
+  int keys_per_split;
+  float c;
+  bool neg;
+};
+
+// Tiled one-pass prefill on MFMA for 16-bit inputs (dtype 1 = f16, 2 = bf16).
+hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
+// The same algorithm with fp32 inputs on the fp32 MFMA.
+hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
+// Split-KV decode: partials then combine, both on stream s.
+hipError_t launch_decode(int dtype, int D, const DecodeArgs& a, hipStream_t s);
+
+}  // namespace attn

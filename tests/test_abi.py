@@ -1,0 +1,118 @@
+"""CPU tests of the C ABI: the library loads, exports what include/attn.h
+declares, and rejects every bad argument before touching the GPU.
+
+Validation calls use fake (never dereferenced) pointers; they return before
+any HIP call, so they run in a container without a GPU.
+"""
+
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "attn.h"
+
+binding = pytest.importorskip("io_aware_softmax_amd.binding")
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def _header_enum(name):
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", HEADER.read_text())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not binding.LIB_PATH.exists():
+        pytest.fail("libattn.so is not built; run __graft_entry__.build()")
+    return binding.load()
+
+
+def test_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(binding.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", str(binding.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_[a-z_]+)\b", out))
+    assert set(declared) <= exported, set(declared) - exported
+    for name in declared:
+        assert hasattr(lib, name)
+    # Nothing beyond the declared API is exported under the attn_ prefix.
+    assert exported == set(declared)
+
+
+def test_header_constants_match_binding():
+    assert _header_enum("ATTN_F32") == binding.ATTN_F32
+    assert _header_enum("ATTN_F16") == binding.ATTN_F16
+    assert _header_enum("ATTN_BF16") == binding.ATTN_BF16
+    assert int(re.search(r"#define ATTN_MAX_SPLITS (\d+)", HEADER.read_text()).group(1)) == binding.ATTN_MAX_SPLITS
+
+
+G = 1 << 40  # fake, far-apart, 16-byte aligned device addresses
+
+
+def _fwd(lib, q=G, k=2 * G, v=3 * G, o=4 * G, lse=5 * G, B=2, H=3, Lq=16, Lk=16, D=64,
+         causal=0, scale=0.125, dtype=2):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, None, dtype)
+
+
+def test_validation_errors(lib):
+    e = {n: _header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_DIM", "ATTN_ERR_UNSUPPORTED_D",
+                                       "ATTN_ERR_DTYPE", "ATTN_ERR_SCALE", "ATTN_ERR_CAUSAL_SHAPE",
+                                       "ATTN_ERR_SPLITS", "ATTN_ERR_ALIAS", "ATTN_ERR_ALIGN")}
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert _fwd(lib, **{kw: 0}) == e["ATTN_ERR_NULL"]
+    for kw in ("B", "H", "Lq", "Lk", "D"):
+        assert _fwd(lib, **{kw: 0}) == e["ATTN_ERR_DIM"]
+        assert _fwd(lib, **{kw: -5}) == e["ATTN_ERR_DIM"]
+    for d in (32, 96, 256, 65, 127):
+        assert _fwd(lib, D=d) == e["ATTN_ERR_UNSUPPORTED_D"]
+    assert _fwd(lib, Lq=(1 << 31) // 64 + 1) == e["ATTN_ERR_DIM"]
+    assert _fwd(lib, Lk=(1 << 30), D=128) == e["ATTN_ERR_DIM"]
+    assert _fwd(lib, B=1 << 16, H=1 << 16) == e["ATTN_ERR_DIM"]
+    for dt in (-1, 3, 99):
+        assert _fwd(lib, dtype=dt) == e["ATTN_ERR_DTYPE"]
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert _fwd(lib, scale=s) == e["ATTN_ERR_SCALE"]
+    assert _fwd(lib, causal=1, Lq=17, Lk=16) == e["ATTN_ERR_CAUSAL_SHAPE"]
+    assert _fwd(lib, o=G) == e["ATTN_ERR_ALIAS"]              # o == q
+    assert _fwd(lib, o=2 * G + 64) == e["ATTN_ERR_ALIAS"]     # o inside k
+    assert _fwd(lib, lse=3 * G + 128) == e["ATTN_ERR_ALIAS"]  # lse inside v
+    assert _fwd(lib, lse=4 * G + 16) == e["ATTN_ERR_ALIAS"]   # lse inside o
+    for kw in ("q", "k", "v", "o"):
+        assert _fwd(lib, **{kw: {"q": G, "k": 2 * G, "v": 3 * G, "o": 4 * G}[kw] + 8}) == e["ATTN_ERR_ALIGN"]
+    assert _fwd(lib, lse=5 * G + 2) == e["ATTN_ERR_ALIGN"]
+    # decode entry point
+    d = lib.attn_decode_fwd
+    assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, -1, None, 2) == e["ATTN_ERR_SPLITS"]
+    assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, 257, None, 2) == e["ATTN_ERR_SPLITS"]
+    assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 48, 0.1, 4, None, 2) == e["ATTN_ERR_UNSUPPORTED_D"]
+    assert d(G, 0, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, 4, None, 2) == e["ATTN_ERR_NULL"]
+    assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 0, 64, 0.1, 4, None, 2) == e["ATTN_ERR_DIM"]
+
+
+def test_strerror_and_auto_splits(lib):
+    for code in range(-10, 1):
+        msg = binding.attn_strerror(code)
+        assert msg and msg != "unknown status"
+    assert binding.attn_strerror(-11) == "unknown status"
+    assert binding.attn_strerror(-10).startswith("HIP error")
+    s = binding.attn_decode_auto_splits(16, 32, 32768, 128)
+    assert 1 <= s <= binding.ATTN_MAX_SPLITS
+    assert binding.attn_decode_auto_splits(1, 1, 4, 64) == 1
+    assert lib.attn_decode_auto_splits(1, 1, 4, 48) == _header_enum("ATTN_ERR_UNSUPPORTED_D")
+    assert lib.attn_decode_auto_splits(0, 1, 4, 64) == _header_enum("ATTN_ERR_DIM")
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(x, x, x)
