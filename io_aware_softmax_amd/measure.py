@@ -1,0 +1,133 @@
+"""Measurement driver: kernels for profilers, copy calibration, length sweep.
+
+Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
+
+* ``kernels`` - uploads the causal bf16 prefill (B1 H32 L8192 D128) and the
+  bf16 decode (B16 H32 Lk32768 D128) inputs and runs each kernel call
+  ``--reps`` times, for rocprofv3 kernel traces and counter passes.
+* ``copy`` - copies a 1 GiB device buffer ``--reps`` times (torch's copy
+  kernel): reads and writes exactly 2^30 bytes per launch, the reference
+  that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
+* ``sweep`` - the fp16 length sweep (B4 H8 D64, L = 64 ... 4096,
+  non-causal): TFLOP/s of ``attn_fwd`` next to a materialised-softmax GPU
+  baseline that writes the scores and weights to device memory (the naive
+  multi-pass algorithm: QK^T, softmax, PV as three torch kernels in fp16,
+  with the transposed operand made contiguous).  Prints one JSON line per L.
+
+Every step of the attention itself runs in libattn.so; torch only provides
+memory, streams, timing events and the comparison baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+from . import binding, inputs
+
+
+def _dev(bits, dtype):
+    if dtype == "f32":
+        return torch.from_numpy(bits).cuda()
+    t = torch.from_numpy(bits.view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
+
+
+def _upload(wl):
+    bits = inputs.generate(wl)
+    return [_dev(bits[t], wl.dtype) for t in "qkv"]
+
+
+def cmd_kernels(args):
+    wp = inputs.WORKLOADS["causal_bf16_8k"]
+    wd = inputs.WORKLOADS["decode_bf16_32k"]
+    q, k, v = _upload(wp)
+    print(f"prefill {wp.name}: {args.reps} launches", flush=True)
+    for _ in range(args.reps):
+        binding.attn_fwd(q, k, v, causal=True, scale=wp.scale)
+    torch.cuda.synchronize()
+    del q, k, v
+    torch.cuda.empty_cache()
+    q, k, v = _upload(wd)
+    splits = binding.attn_decode_auto_splits(wd.B, wd.H, wd.Lk, wd.D)
+    print(f"decode {wd.name}: {args.reps} launches, {splits} splits", flush=True)
+    for _ in range(args.reps):
+        binding.attn_decode_fwd(q, k, v, scale=wd.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    print("done", flush=True)
+
+
+def cmd_copy(args):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    print(f"copy: {args.reps} launches of {n} bytes", flush=True)
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("done", flush=True)
+
+
+def _time(fn, reps, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return float(np.median(ms)), float(ms[0])
+
+
+def _materialised(q, k, v, scale):
+    # Scores and weights are written to device memory between the kernels.
+    s = torch.matmul(q, k.transpose(-2, -1).contiguous()) * scale
+    p = torch.softmax(s, dim=-1)
+    return torch.matmul(p, v)
+
+
+def cmd_sweep(args):
+    for L in inputs.SWEEP_LENGTHS:
+        wl = inputs.WORKLOADS[f"sweep_f16_L{L}"]
+        q, k, v = _upload(wl)
+        o = torch.empty_like(q)
+        lse = torch.empty(wl.B, wl.H, L, dtype=torch.float32, device="cuda")
+        ours = _time(lambda: binding.attn_fwd(q, k, v, causal=False, scale=wl.scale, out=o, lse=lse), args.reps)
+        base = _time(lambda: _materialised(q, k, v, wl.scale), args.reps)
+        ref = _materialised(q, k, v, wl.scale)
+        torch.cuda.synchronize()
+        diff = float((o.float() - ref.float()).abs().max())
+        rec = {"workload": wl.name, "L": L, "flops": wl.flops(),
+               "attn_fwd_ms": ours[0], "attn_fwd_tflops": wl.flops() / ours[0] / 1e9,
+               "materialised_ms": base[0], "materialised_tflops": wl.flops() / base[0] / 1e9,
+               "speedup": base[0] / ours[0], "max_abs_diff_vs_materialised": diff}
+        print(json.dumps(rec), flush=True)
+        del q, k, v, o, lse, ref
+        torch.cuda.empty_cache()
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("cmd", choices=["kernels", "copy", "sweep"])
+    p.add_argument("--reps", type=int, default=5)
+    args = p.parse_args(argv)
+    if not torch.cuda.is_available():
+        print("needs a GPU", file=sys.stderr)
+        return 1
+    binding.load()
+    {"kernels": cmd_kernels, "copy": cmd_copy, "sweep": cmd_sweep}[args.cmd](args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
