@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_internal.hpp"
 
@@ -47,19 +48,31 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // key rows per tile
 constexpr int NT = 256;  // threads per workgroup
+// Largest lag (base 2) of the reference maximum behind the true running
+// maximum: weights exp(a - d) stay below 2^8.
+constexpr float kTau = 8.f;
 
 template <int D>
 struct Tile {
-  // LDS row pitches.  K: +16 B so that 16 lanes reading 16 B each from 16
-  // consecutive rows hit 16 disjoint 4-bank groups.  V: +64 B so that the
-  // four rows of one transposed read land in four disjoint 16-bank groups.
-  static constexpr int KPITCH = D * 2 + 16;
-  static constexpr int VPITCH = D * 2 + 64;
-  static constexpr int KBYTES = BN * KPITCH;
-  static constexpr int STAGE = KBYTES + BN * VPITCH;
-  static constexpr int CHUNKS = BN * D / 8 / NT;  // 16-byte chunks per thread per tensor
+  // K and V tiles are stored row-major without padding; the 16-byte chunk c
+  // of row r sits at chunk position c ^ swz(r).  The swizzle makes both LDS
+  // read patterns conflict-free: 16 lanes reading the same chunk of 16
+  // consecutive rows (K, ds_read_b128), and the 4 rows x 4 chunks of one
+  // half-wave transposed read (V, ds_read_b64_tr_b16).
+  static constexpr int ROWB = D * 2;              // bytes per row
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int TBYTES = BN * ROWB;        // one tensor tile
+  static constexpr int STAGE = 2 * TBYTES;        // K tile then V tile
+  static constexpr int CHUNKS = TBYTES / 16 / NT; // 16-byte chunks per thread per tensor
   static constexpr int KSTEPS = D / 16;           // MFMA k-steps of Q K^T
   static constexpr int DBLK = D / 32;             // 32-wide blocks of the output
+  __device__ static constexpr int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  // Byte offset of element column `col` (a multiple of 4) of row r.
+  __device__ static constexpr int off(int r, int col) {
+    return r * ROWB + ((((col >> 3) ^ swz(r))) << 4) + ((col & 7) << 1);
+  }
 };
 
 template <bool BF16>
@@ -105,7 +118,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int nqt, float c, unsigned qsign) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE];
+  // Two pipeline stages in separate arrays so that the compiler can tell the
+  // stage being filled by DMA from the stage being read.
+  __shared__ __attribute__((aligned(16))) char stage0[T::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,135 +163,177 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
 
-  // Staging registers for the next K/V tile.
-  u32x4 kst[T::CHUNKS], vst[T::CHUNKS];
-  auto gload = [&](int kv0) {
+  // K/V tiles go HBM -> LDS by DMA (global_load_lds_dwordx4): one
+  // instruction moves 64 lanes x 16 B into 1 KB of consecutive LDS; lane l
+  // fetches the global chunk that the swizzle places in slot l.  Rows past
+  // Lk read row Lk-1 (in bounds) and their V slots are zeroed afterwards.
+  // Per-lane source offsets (bytes within a tile) are computed once.
+  unsigned src_off[T::CHUNKS];
+  int src_row[T::CHUNKS];
+#pragma unroll
+  for (int u = 0; u < T::CHUNKS; ++u) {
+    const int slot = (u * (NT / 64) + w) * 64 + lane;
+    src_row[u] = slot / T::CPR;
+    src_off[u] = src_row[u] * T::ROWB + (((slot % T::CPR) ^ T::swz(src_row[u])) << 4);
+  }
+  const char* Kb = reinterpret_cast<const char*>(Kh);
+  const char* Vb = reinterpret_cast<const char*>(Vh);
+  auto dma = [&](char* stage, int kv0) {
+    const bool full = kv0 + BN <= Lk;
+    const unsigned tile_off = (unsigned)kv0 * T::ROWB;
 #pragma unroll
     for (int u = 0; u < T::CHUNKS; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / (D / 8), col = ci % (D / 8);
-      const int key = kv0 + row;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key < Lk) {
-        kx = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col * 8);
-        vx = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + col * 8);
-      }
-      kst[u] = kx;
-      vst[u] = vx;
+      unsigned o = tile_off + src_off[u];
+      if (!full && kv0 + src_row[u] >= Lk)  // clamp to row Lk-1, same chunk
+        o = (unsigned)(Lk - 1) * T::ROWB + (src_off[u] % T::ROWB);
+      char* dst = stage + (u * (NT / 64) + w) * 1024;
+      __builtin_amdgcn_global_load_lds(Kb + o, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vb + o, (__attribute__((address_space(3))) void*)(dst + T::TBYTES),
+                                       16, 0, 0);
     }
   };
-  auto sstore = [&](int stage) {
-    char* base = smem + stage * T::STAGE;
+  // Wait for this thread's DMA, then zero the V slots of rows past Lk.
+  auto land = [&](char* stage, int kv0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kv0 + BN > Lk) {
 #pragma unroll
-    for (int u = 0; u < T::CHUNKS; ++u) {
-      const int ci = tid + NT * u;
-      const int row = ci / (D / 8), col = ci % (D / 8);
-      *reinterpret_cast<u32x4*>(base + row * T::KPITCH + col * 16) = kst[u];
-      *reinterpret_cast<u32x4*>(base + T::KBYTES + row * T::VPITCH + col * 16) = vst[u];
+      for (int u = 0; u < T::CHUNKS; ++u) {
+        if (kv0 + src_row[u] >= Lk)
+          *reinterpret_cast<u32x4*>(stage + T::TBYTES + ((u * (NT / 64) + w) * 64 + lane) * 16) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
   f32x16 oacc[T::DBLK];
 #pragma unroll
   for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max, base-2 scaled-score units
-  float l_run = 0.f;        // this lane's part of the running denominator
+  // Reference maximum d of the row (base-2 scaled-score units) and this
+  // lane's part of the denominator s, both relative to that reference.
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
 
   // Tile row read by this lane for S^T: bits 2 and 3 of n swapped, so the
   // accumulator register r of block blk holds key 32 blk + 16 (r/8) + 8 h + r%8.
   const int prow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
   const int g = lane >> 4, li = lane & 15;
 
-  if (nkv > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  // One key tile.  MASK selects the variant for tiles that hold masked keys
+  // (the causal diagonal band and the Lk tail); all other tiles run without
+  // any per-score masking work.
+  auto tile = [&](const char* Ks, const char* Vs, int kv0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
 
-  for (int j = 0; j < nkv; ++j) {
-    const int kv0 = j * BN;
-    if (j + 1 < nkv) gload(kv0 + BN);
-
-    if (wave_live && kv0 < w_key_end) {
-      const char* Ks = smem + (j & 1) * T::STAGE;
-      const char* Vs = Ks + T::KBYTES;
-
-      // ---- scores S^T = K_j Q^T (two 32-key blocks) ----
-      f32x16 sacc[2];
+    // ---- scores S^T = K_j Q^T (two 32-key blocks); fragments read ahead ----
+    f32x16 sacc[2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        sacc[blk] = f32x16{};
-        const char* kp = Ks + (32 * blk + prow) * T::KPITCH + 16 * h;
+    for (int blk = 0; blk < 2; ++blk) {
+      const int krow = 32 * blk + prow;
+      s16x8 kf[T::KSTEPS];
 #pragma unroll
-        for (int t = 0; t < T::KSTEPS; ++t)
-          sacc[blk] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(kp + 32 * t), qreg[t], sacc[blk]);
-      }
+      for (int t = 0; t < T::KSTEPS; ++t)
+        kf[t] = *reinterpret_cast<const s16x8*>(Ks + T::off(krow, 16 * t + 8 * h));
+      sacc[blk] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < T::KSTEPS; ++t) sacc[blk] = mfma32<BF16>(kf[t], qreg[t], sacc[blk]);
+    }
 
-      // ---- mask: keys past Lk, and keys after the diagonal (causal) ----
-      const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
-      unsigned live = 0xffffffffu;
-      if (need_mask) {
-        live = 0u;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * blk + 16 * (r >> 3) + 8 * h + (r & 7);
-            const bool ok = key < Lk && (!CAUSAL || key <= qi + off);
-            live |= (ok ? 1u : 0u) << (16 * blk + r);
-            if (!ok) sacc[blk][r] = -INFINITY;
-          }
-      }
-
-      // ---- running max (guide: d_k = max(d_{k-1}, max of chunk k)) ----
-      float mx = -INFINITY;
+    // ---- mask: keys past Lk, and keys after the diagonal (causal) ----
+    unsigned live = 0xffffffffu;
+    if constexpr (MASK) {
+      live = 0u;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
-      mx = halves_max(mx);
-      const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      // Correction of the old state: exp(d_{k-1} - d_k) (0 on the first tile).
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-
-      // ---- P = exp(a - d_k): fp32 into the denominator, rounded for the MFMA ----
-      s16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int blk = s >> 1, r = 8 * (s & 1) + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][r], c, -m_use));
-          if (need_mask && !((live >> (16 * blk + r)) & 1u)) p = 0.f;
-          pb[s][e] = (short)round16<BF16>(p);
-          psum += p;  // the denominator keeps fp32 weights (exact LSE)
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * blk + 16 * (r >> 3) + 8 * h + (r & 7);
+          const bool ok = key < Lk && (!CAUSAL || key <= qi + off);
+          live |= (ok ? 1u : 0u) << (16 * blk + r);
+          if (!ok) sacc[blk][r] = -INFINITY;
         }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
-
-      // ---- O^T += V_j^T P^T ----
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int db = 0; db < T::DBLK; ++db) {
-          const char* vp = Vs + (16 * s + 8 * h + (li >> 2)) * T::VPITCH +
-                           (32 * db + 16 * (g & 1) + 4 * (li & 3)) * 2;
-          const s16x4 lo = lds_read_tr(vp);
-          const s16x4 hi = lds_read_tr(vp + 4 * T::VPITCH);
-          const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[db] = mfma32<BF16>(a, pb[s], oacc[db]);
-        }
-      }
     }
 
-    if (j + 1 < nkv) sstore((j + 1) & 1);
+    // ---- running maximum (guide: d_k = max(d_{k-1}, max of chunk k)) ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
+    mx = halves_max(mx);
+    const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+    // The reference d moves to the new maximum only when the tile's maximum
+    // exceeds it by more than kTau (base 2); then O~ and s are corrected by
+    // exp(d_old - d_new) as in the guide.  Otherwise d stays, the weights
+    // exp(a - d) are at most 2^kTau, and O~ / s is unchanged in real
+    // arithmetic (the correction holds for any reference).  The check is per
+    // row; the branch is taken by the whole wave if any row needs it.
+    const bool grow = m_tile > m_ref + kTau;
+    if (__any(grow)) {
+      const float m_new = grow ? m_tile : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+
+    // ---- P = exp(a - d): fp32 into the denominator, rounded for the MFMA ----
+    s16x8 pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int blk = st >> 1, r = 8 * (st & 1) + e;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][r], c, -m_use));
+        if constexpr (MASK) p = ((live >> (16 * blk + r)) & 1u) ? p : 0.f;
+        pb[st][e] = (short)round16<BF16>(p);
+        psum += p;  // the denominator keeps fp32 weights (exact LSE)
+      }
+    }
+    l_run += psum;
+
+    // ---- O^T += V_j^T P^T; V^T fragments via transposed LDS reads ----
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      s16x8 vf[T::DBLK];
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) {
+        const int vrow = 16 * st + 8 * h + (li >> 2);
+        const int vcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
+        const s16x4 lo = lds_read_tr(Vs + T::off(vrow, vcol));
+        const s16x4 hi = lds_read_tr(Vs + T::off(vrow + 4, vcol));
+        vf[db] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int db = 0; db < T::DBLK; ++db) oacc[db] = mfma32<BF16>(vf[db], pb[st], oacc[db]);
+    }
+  };
+
+  // One pipeline step: start the DMA of tile j+1 into `nxt`, compute tile j
+  // from `cur`, wait for the DMA, then one barrier for the workgroup.
+  auto step = [&](int j, char* cur, char* nxt) {
+    const int kv0 = j * BN;
+    const bool more = j + 1 < nkv;
+    if (more) dma(nxt, kv0 + BN);
+    if (wave_live && kv0 < w_key_end) {
+      const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
+      if (need_mask)
+        tile(cur, cur + T::TBYTES, kv0, std::integral_constant<bool, true>{});
+      else
+        tile(cur, cur + T::TBYTES, kv0, std::integral_constant<bool, false>{});
+    }
+    if (more) land(nxt, kv0 + BN);
     __syncthreads();
+  };
+
+  dma(stage0, 0);
+  land(stage0, 0);
+  __syncthreads();
+  for (int j = 0; j < nkv; j += 2) {
+    step(j, stage0, stage1);
+    if (j + 1 < nkv) step(j + 1, stage1, stage0);
   }
 
   // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
@@ -294,7 +352,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
                             ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(Oq + d) = make_uint2(lo, hi);
       }
-    if (h == 0) LSE[(size_t)bh * Lq + qi] = (m_run + log2f(l_tot)) * kLn2;
+    if (h == 0) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
   }
 }
 
