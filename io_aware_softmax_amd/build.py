@@ -51,7 +51,10 @@ def build(verbose: bool = False) -> Path:
             if m.strip():
                 print(m, file=sys.stderr)
     tmp = LIB.with_suffix(".so.tmp")
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", str(tmp), *[str(o) for o, _ in jobs]])
+    # --no-undefined: a kernel whose host stub was not emitted must fail the
+    # build, not the first launch.
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-Wl,--no-undefined", "-o", str(tmp),
+          *[str(o) for o, _ in jobs]])
     os.replace(tmp, LIB)
     return LIB
 

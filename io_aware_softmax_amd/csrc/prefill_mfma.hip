@@ -48,31 +48,34 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // key rows per tile
 constexpr int NT = 256;  // threads per workgroup
+constexpr int NW = NT / 64;  // waves per workgroup
 // Largest lag (base 2) of the reference maximum behind the true running
 // maximum: weights exp(a - d) stay below 2^8.
 constexpr float kTau = 8.f;
 
 template <int D>
 struct Tile {
-  // K and V tiles are stored row-major without padding; the 16-byte chunk c
-  // of row r sits at chunk position c ^ swz(r).  The swizzle makes both LDS
-  // read patterns conflict-free: 16 lanes reading the same chunk of 16
-  // consecutive rows (K, ds_read_b128), and the 4 rows x 4 chunks of one
-  // half-wave transposed read (V, ds_read_b64_tr_b16).
-  static constexpr int ROWB = D * 2;              // bytes per row
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int TBYTES = BN * ROWB;        // one tensor tile
-  static constexpr int STAGE = 2 * TBYTES;        // K tile then V tile
-  static constexpr int CHUNKS = TBYTES / 16 / NT; // 16-byte chunks per thread per tensor
-  static constexpr int KSTEPS = D / 16;           // MFMA k-steps of Q K^T
-  static constexpr int DBLK = D / 32;             // 32-wide blocks of the output
-  __device__ static constexpr int swz(int r) {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-  }
-  // Byte offset of element column `col` (a multiple of 4) of row r.
-  __device__ static constexpr int off(int r, int col) {
-    return r * ROWB + ((((col >> 3) ^ swz(r))) << 4) + ((col & 7) << 1);
-  }
+  // LDS rows are padded so that every read address is a lane base plus an
+  // immediate offset, and both read patterns are bank-conflict-free:
+  //  K: pitch = D*2 + 16 B (an odd number of 16-byte slots): 16 lanes
+  //     reading one 16-byte chunk of 16 consecutive rows hit 16 different
+  //     4-bank groups (ds_read_b128).
+  //  V: pitch = D*2 + 64 B (4 mod 16 slots): the 4 rows x 64 B of one
+  //     half-wave transposed read (ds_read_b64_tr_b16) hit disjoint banks.
+  static constexpr int CPR = D / 8;                 // 16-byte data chunks per row
+  static constexpr int KSPR = CPR + 1;              // K slots per row (1 pad slot)
+  static constexpr int VSPR = CPR + 4;              // V slots per row (4 pad slots)
+  static constexpr int KPITCH = KSPR * 16;
+  static constexpr int VPITCH = VSPR * 16;
+  static constexpr int KBYTES = BN * KPITCH;
+  static constexpr int STAGE = KBYTES + BN * VPITCH;
+  static constexpr int KINST = BN * KSPR / 64;      // 64-lane DMA instructions per K tile
+  static constexpr int VINST = BN * VSPR / 64;      // ... per V tile
+  static constexpr int KSTEPS = D / 16;             // MFMA k-steps of Q K^T
+  static constexpr int DBLK = D / 32;               // 32-wide blocks of the output
+  static constexpr int KI = (KINST + NW - 1) / NW;  // K DMA instructions per wave
+  static constexpr int VI = (VINST + NW - 1) / NW;  // V DMA instructions per wave
+  static_assert(BN * KSPR % 64 == 0 && BN * VSPR % 64 == 0, "whole DMA instructions");
 };
 
 template <bool BF16>
@@ -107,9 +110,54 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+__device__ __forceinline__ __attribute__((address_space(3))) void* to_lds(char* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+
+// K/V tiles go HBM -> LDS by DMA (global_load_lds_dwordx4): one instruction
+// moves 64 lanes x 16 B into 1 KB of consecutive LDS, here a run of 16-byte
+// slots of the padded tile.  Lane l of DMA instruction i fills slot 64 i + l
+// (row = slot / slots-per-row, chunk = the rest); pad slots fetch chunk 0 of
+// their row again (in bounds, never read).  Wave w issues instructions w,
+// w + 4, ...
+//
+// Byte offset, within one tile of the source tensor, of the chunk that lane
+// `lane` fetches for DMA instruction `inst` of a tile with `spr` slots per
+// row.
+template <int D>
+__device__ __forceinline__ unsigned dma_src_offset(int inst, int lane, int spr) {
+  const int slot = inst * 64 + lane;
+  const int row = slot / spr;
+  const int chunk = slot - row * spr;
+  return (unsigned)row * (D * 2) + (unsigned)(chunk < D / 8 ? chunk : 0) * 16;
+}
+
+// Rows at or past `rows_left` (keys past Lk) are redirected to row
+// rows_left - 1 of the tile, which is in bounds.
+template <int D>
+__device__ __forceinline__ unsigned dma_clamp(unsigned off, int rows_left) {
+  const int row = (int)(off / (D * 2));
+  return row < rows_left ? off : (unsigned)(rows_left - 1) * (D * 2) + off % (D * 2);
+}
+
+// Issue this wave's DMA instructions for one tile of one tensor.
+template <int D, int INST, int PER_WAVE>
+__device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, const unsigned* src_off,
+                                         int w, bool full, int rows_left) {
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = i * NW + w;
+    if (inst < INST) {
+      const unsigned o = full ? src_off[i] : dma_clamp<D>(src_off[i], rows_left);
+      __builtin_amdgcn_global_load_lds(src_tile + o, to_lds(dst_tile + inst * 1024), 16, 0, 0);
+    }
+  }
 }
 
 template <bool BF16, int D, bool CAUSAL>
@@ -125,7 +173,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int n = lane & 31;  // query column of the S^T / O^T tiles owned by this lane
   const int h = lane >> 5;  // which 8-wide k slice this lane feeds to the MFMA
 
@@ -163,44 +211,32 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
 
-  // K/V tiles go HBM -> LDS by DMA (global_load_lds_dwordx4): one
-  // instruction moves 64 lanes x 16 B into 1 KB of consecutive LDS; lane l
-  // fetches the global chunk that the swizzle places in slot l.  Rows past
-  // Lk read row Lk-1 (in bounds) and their V slots are zeroed afterwards.
-  // Per-lane source offsets (bytes within a tile) are computed once.
-  unsigned src_off[T::CHUNKS];
-  int src_row[T::CHUNKS];
-#pragma unroll
-  for (int u = 0; u < T::CHUNKS; ++u) {
-    const int slot = (u * (NT / 64) + w) * 64 + lane;
-    src_row[u] = slot / T::CPR;
-    src_off[u] = src_row[u] * T::ROWB + (((slot % T::CPR) ^ T::swz(src_row[u])) << 4);
-  }
+  // K/V tiles go HBM -> LDS by DMA (see dma_tile).  Rows past Lk read row
+  // Lk-1 (in bounds) and their V slots are zeroed once the DMA has landed.
   const char* Kb = reinterpret_cast<const char*>(Kh);
   const char* Vb = reinterpret_cast<const char*>(Vh);
+  unsigned k_src[T::KI];
+  unsigned v_src[T::VI];
+#pragma unroll
+  for (int i = 0; i < T::KI; ++i) k_src[i] = dma_src_offset<D>(i * NW + w, lane, T::KSPR);
+#pragma unroll
+  for (int i = 0; i < T::VI; ++i) v_src[i] = dma_src_offset<D>(i * NW + w, lane, T::VSPR);
   auto dma = [&](char* stage, int kv0) {
     const bool full = kv0 + BN <= Lk;
-    const unsigned tile_off = (unsigned)kv0 * T::ROWB;
-#pragma unroll
-    for (int u = 0; u < T::CHUNKS; ++u) {
-      unsigned o = tile_off + src_off[u];
-      if (!full && kv0 + src_row[u] >= Lk)  // clamp to row Lk-1, same chunk
-        o = (unsigned)(Lk - 1) * T::ROWB + (src_off[u] % T::ROWB);
-      char* dst = stage + (u * (NT / 64) + w) * 1024;
-      __builtin_amdgcn_global_load_lds(Kb + o, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vb + o, (__attribute__((address_space(3))) void*)(dst + T::TBYTES),
-                                       16, 0, 0);
-    }
+    const size_t base = (size_t)kv0 * (D * 2);  // uniform tile offset
+    dma_tile<D, T::KINST, T::KI>(Kb + base, stage, k_src, w, full, Lk - kv0);
+    dma_tile<D, T::VINST, T::VI>(Vb + base, stage + T::KBYTES, v_src, w, full, Lk - kv0);
   };
   // Wait for this thread's DMA, then zero the V slots of rows past Lk.
   auto land = [&](char* stage, int kv0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (kv0 + BN > Lk) {
 #pragma unroll
-      for (int u = 0; u < T::CHUNKS; ++u) {
-        if (kv0 + src_row[u] >= Lk)
-          *reinterpret_cast<u32x4*>(stage + T::TBYTES + ((u * (NT / 64) + w) * 64 + lane) * 16) =
-              u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < T::VI; ++i) {
+        const int inst = i * NW + w;
+        const int slot = inst * 64 + lane;
+        if (inst < T::VINST && kv0 + slot / T::VSPR >= Lk)
+          *reinterpret_cast<u32x4*>(stage + T::KBYTES + slot * 16) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -224,19 +260,20 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   auto tile = [&](const char* Ks, const char* Vs, int kv0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
 
-    // ---- scores S^T = K_j Q^T (two 32-key blocks); fragments read ahead ----
+    // ---- scores S^T = K_j Q^T (two 32-key blocks) ----
     f32x16 sacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int krow = 32 * blk + prow;
-      s16x8 kf[T::KSTEPS];
-#pragma unroll
-      for (int t = 0; t < T::KSTEPS; ++t)
-        kf[t] = *reinterpret_cast<const s16x8*>(Ks + T::off(krow, 16 * t + 8 * h));
+      const char* kp = Ks + (32 * blk + prow) * T::KPITCH + 16 * h;
       sacc[blk] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < T::KSTEPS; ++t) sacc[blk] = mfma32<BF16>(kf[t], qreg[t], sacc[blk]);
+      for (int t = 0; t < T::KSTEPS; ++t)
+        sacc[blk] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(kp + 32 * t), qreg[t], sacc[blk]);
     }
+
+    // Phase fences: keep the scheduler from stretching live ranges across
+    // the score, softmax and value phases (the register file is full).
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- mask: keys past Lk, and keys after the diagonal (causal) ----
     unsigned live = 0xffffffffu;
@@ -293,17 +330,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
       }
     }
     l_run += psum;
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V_j^T P^T; V^T fragments via transposed LDS reads ----
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      if (st) __builtin_amdgcn_sched_barrier(0);
       s16x8 vf[T::DBLK];
 #pragma unroll
       for (int db = 0; db < T::DBLK; ++db) {
-        const int vrow = 16 * st + 8 * h + (li >> 2);
-        const int vcol = 32 * db + 16 * (g & 1) + 4 * (li & 3);
-        const s16x4 lo = lds_read_tr(Vs + T::off(vrow, vcol));
-        const s16x4 hi = lds_read_tr(Vs + T::off(vrow + 4, vcol));
+        const char* vp = Vs + (16 * st + 8 * h + (li >> 2)) * T::VPITCH +
+                         (32 * db + 16 * (g & 1) + 4 * (li & 3)) * 2;
+        const s16x4 lo = lds_read_tr(vp);
+        const s16x4 hi = lds_read_tr(vp + 4 * T::VPITCH);
         vf[db] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
@@ -311,29 +350,42 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     }
   };
 
-  // One pipeline step: start the DMA of tile j+1 into `nxt`, compute tile j
-  // from `cur`, wait for the DMA, then one barrier for the workgroup.
-  auto step = [&](int j, char* cur, char* nxt) {
-    const int kv0 = j * BN;
-    const bool more = j + 1 < nkv;
-    if (more) dma(nxt, kv0 + BN);
-    if (wave_live && kv0 < w_key_end) {
-      const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
-      if (need_mask)
-        tile(cur, cur + T::TBYTES, kv0, std::integral_constant<bool, true>{});
-      else
-        tile(cur, cur + T::TBYTES, kv0, std::integral_constant<bool, false>{});
-    }
-    if (more) land(nxt, kv0 + BN);
-    __syncthreads();
-  };
+  // Tiles [0, j_mask) of this wave hold no masked key; tiles from j_mask on
+  // (the causal diagonal band of the wave's rows, the Lk tail) do.  Two
+  // loops instead of a per-tile choice keep the accumulators in one set of
+  // registers.  Every wave runs nkv steps, so barriers stay matched.
+  int j_mask = nkv;
+  if (CAUSAL) {
+    // first tile whose last key lies past the diagonal of the wave's first row
+    const int first_bad = wq0 + off - BN + 2;
+    j_mask = first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN;
+  }
+  if (Lk % BN) j_mask = min(j_mask, Lk / BN);
+  j_mask = __builtin_amdgcn_readfirstlane(min(j_mask, nkv));
 
   dma(stage0, 0);
   land(stage0, 0);
   __syncthreads();
-  for (int j = 0; j < nkv; j += 2) {
-    step(j, stage0, stage1);
-    if (j + 1 < nkv) step(j + 1, stage1, stage0);
+  // One pipeline step per tile j: start the DMA of tile j+1 into the other
+  // stage, compute tile j, wait for the DMA, then one workgroup barrier.
+  int j = 0;
+  for (; j < j_mask; ++j) {
+    char* cur = (j & 1) ? stage1 : stage0;
+    char* nxt = (j & 1) ? stage0 : stage1;
+    const int kv0 = j * BN;
+    if (j + 1 < nkv) dma(nxt, kv0 + BN);
+    if (wave_live) tile(cur, cur + T::KBYTES, kv0, std::integral_constant<bool, false>{});
+    if (j + 1 < nkv) land(nxt, kv0 + BN);
+    __syncthreads();
+  }
+  for (; j < nkv; ++j) {
+    char* cur = (j & 1) ? stage1 : stage0;
+    char* nxt = (j & 1) ? stage0 : stage1;
+    const int kv0 = j * BN;
+    if (j + 1 < nkv) dma(nxt, kv0 + BN);
+    if (wave_live && kv0 < w_key_end) tile(cur, cur + T::KBYTES, kv0, std::integral_constant<bool, true>{});
+    if (j + 1 < nkv) land(nxt, kv0 + BN);
+    __syncthreads();
   }
 
   // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
