@@ -68,7 +68,7 @@ struct Tile {
   static constexpr int KPITCH = KSPR * 16;
   static constexpr int VPITCH = VSPR * 16;
   static constexpr int KBYTES = BN * KPITCH;
-  static constexpr int STAGE = KBYTES + BN * VPITCH;
+  static constexpr int VBYTES = BN * VPITCH;
   static constexpr int KINST = BN * KSPR / 64;      // 64-lane DMA instructions per K tile
   static constexpr int VINST = BN * VSPR / 64;      // ... per V tile
   static constexpr int KSTEPS = D / 16;             // MFMA k-steps of Q K^T
@@ -146,6 +146,22 @@ __device__ __forceinline__ unsigned dma_clamp(unsigned off, int rows_left) {
   return row < rows_left ? off : (unsigned)(rows_left - 1) * (D * 2) + off % (D * 2);
 }
 
+// One global_load_lds_dwordx4: 16 bytes per lane from src_base + voff into
+// LDS at lds_base + 16 * lane.  Written as inline assembly so that the
+// compiler's LGKM wait model does not count it: with the builtin, every wait
+// for an LDS read becomes a wait for all outstanding LDS traffic including
+// this DMA.  Completion is awaited explicitly with s_waitcnt vmcnt(0).
+__device__ __forceinline__ void dma16(const char* src_base, unsigned voff, char* lds_base) {
+  const unsigned lds = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1\n"
+      :
+      : "v"(voff), "s"(src_base), "s"(lds)
+      : "memory", "m0");
+}
+
 // Issue this wave's DMA instructions for one tile of one tensor.
 template <int D, int INST, int PER_WAVE>
 __device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, const unsigned* src_off,
@@ -155,7 +171,7 @@ __device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, c
     const int inst = i * NW + w;
     if (inst < INST) {
       const unsigned o = full ? src_off[i] : dma_clamp<D>(src_off[i], rows_left);
-      __builtin_amdgcn_global_load_lds(src_tile + o, to_lds(dst_tile + inst * 1024), 16, 0, 0);
+      dma16(src_tile, o, dst_tile + inst * 1024);
     }
   }
 }
@@ -166,10 +182,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int nqt, float c, unsigned qsign) {
   using T = Tile<D>;
-  // Two pipeline stages in separate arrays so that the compiler can tell the
-  // stage being filled by DMA from the stage being read.
-  __shared__ __attribute__((aligned(16))) char stage0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1[T::STAGE];
+  // K tiles and V tiles are double buffered in their own arrays, one tile out
+  // of phase: step j reads K_{j+1} and V_j while K_{j+2} and V_{j+1} land.
+  __shared__ __attribute__((aligned(16))) char kb0[T::KBYTES];
+  __shared__ __attribute__((aligned(16))) char kb1[T::KBYTES];
+  __shared__ __attribute__((aligned(16))) char vb0[T::VBYTES];
+  __shared__ __attribute__((aligned(16))) char vb1[T::VBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -190,15 +208,24 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   const int off = Lk - Lq;  // bottom-right causal alignment
 
   const unsigned short* Qh = Q + (size_t)bh * Lq * D;
-  const unsigned short* Kh = K + (size_t)bh * Lk * D;
-  const unsigned short* Vh = V + (size_t)bh * Lk * D;
+  const char* Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
+  const char* Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
 
   const int q_last = min(q0 + BM, Lq) - 1;
   const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
-  const int nkv = (kv_end + BN - 1) / BN;
-  const int wq0 = q0 + 32 * w;  // first query of this wave
-  const bool wave_live = wq0 < Lq;
+  const int nkv = (kv_end + BN - 1) / BN;  // tiles the workgroup streams
+  const int wq0 = q0 + 32 * w;             // first query of this wave
   const int w_key_end = CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk;
+  // Tiles [0, w_nkv) are computed by this wave; tiles [0, j_mask) hold no
+  // masked key for it (the causal diagonal band and the Lk tail do).
+  const int w_nkv = __builtin_amdgcn_readfirstlane(wq0 < Lq ? (w_key_end + BN - 1) / BN : 0);
+  int j_mask = w_nkv;
+  if (CAUSAL) {
+    const int first_bad = wq0 + off - BN + 2;  // first kv0 whose last key passes the diagonal
+    j_mask = min(j_mask, first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN);
+  }
+  if (Lk % BN) j_mask = min(j_mask, Lk / BN);
+  j_mask = __builtin_amdgcn_readfirstlane(j_mask);
 
   // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
   const int qi = wq0 + n;
@@ -211,24 +238,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
 
-  // K/V tiles go HBM -> LDS by DMA (see dma_tile).  Rows past Lk read row
-  // Lk-1 (in bounds) and their V slots are zeroed once the DMA has landed.
-  const char* Kb = reinterpret_cast<const char*>(Kh);
-  const char* Vb = reinterpret_cast<const char*>(Vh);
+  // DMA of one K or V tile (see dma_tile); rows past Lk read row Lk-1 and
+  // the V slots of those rows are zeroed once the DMA has landed.
   unsigned k_src[T::KI];
   unsigned v_src[T::VI];
 #pragma unroll
   for (int i = 0; i < T::KI; ++i) k_src[i] = dma_src_offset<D>(i * NW + w, lane, T::KSPR);
 #pragma unroll
   for (int i = 0; i < T::VI; ++i) v_src[i] = dma_src_offset<D>(i * NW + w, lane, T::VSPR);
-  auto dma = [&](char* stage, int kv0) {
-    const bool full = kv0 + BN <= Lk;
-    const size_t base = (size_t)kv0 * (D * 2);  // uniform tile offset
-    dma_tile<D, T::KINST, T::KI>(Kb + base, stage, k_src, w, full, Lk - kv0);
-    dma_tile<D, T::VINST, T::VI>(Vb + base, stage + T::KBYTES, v_src, w, full, Lk - kv0);
+  auto dma_k = [&](char* buf, int kv0) {
+    dma_tile<D, T::KINST, T::KI>(Kb + (size_t)kv0 * (D * 2), buf, k_src, w, kv0 + BN <= Lk, Lk - kv0);
   };
-  // Wait for this thread's DMA, then zero the V slots of rows past Lk.
-  auto land = [&](char* stage, int kv0) {
+  auto dma_v = [&](char* buf, int kv0) {
+    dma_tile<D, T::VINST, T::VI>(Vb + (size_t)kv0 * (D * 2), buf, v_src, w, kv0 + BN <= Lk, Lk - kv0);
+  };
+  auto land = [&](char* vbuf, int kv0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (kv0 + BN > Lk) {
 #pragma unroll
@@ -236,7 +260,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
         const int inst = i * NW + w;
         const int slot = inst * 64 + lane;
         if (inst < T::VINST && kv0 + slot / T::VSPR >= Lk)
-          *reinterpret_cast<u32x4*>(stage + T::KBYTES + slot * 16) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -254,56 +278,53 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   const int prow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
   const int g = lane >> 4, li = lane & 15;
 
-  // One key tile.  MASK selects the variant for tiles that hold masked keys
-  // (the causal diagonal band and the Lk tail); all other tiles run without
-  // any per-score masking work.
-  auto tile = [&](const char* Ks, const char* Vs, int kv0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-
-    // ---- scores S^T = K_j Q^T (two 32-key blocks) ----
-    f32x16 sacc[2];
+  // ---- building blocks of one tile ----
+  // S^T = K Q^T for the 64 keys of a K tile (two 32-key blocks, 16 MFMAs).
+  // The two blocks alternate so consecutive MFMAs never wait on each other.
+  auto scores = [&](f32x16 (&s)[2], const char* Ks) {
+    const char* kp = Ks + prow * T::KPITCH + 16 * h;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const char* kp = Ks + (32 * blk + prow) * T::KPITCH + 16 * h;
-      sacc[blk] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < T::KSTEPS; ++t)
-        sacc[blk] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(kp + 32 * t), qreg[t], sacc[blk]);
-    }
-
-    // Phase fences: keep the scheduler from stretching live ranges across
-    // the score, softmax and value phases (the register file is full).
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- mask: keys past Lk, and keys after the diagonal (causal) ----
-    unsigned live = 0xffffffffu;
-    if constexpr (MASK) {
-      live = 0u;
+    for (int t = 0; t < T::KSTEPS; ++t)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
+        s[blk] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(kp + 32 * blk * T::KPITCH + 32 * t), qreg[t],
+                              s[blk]);
+  };
+  // Keys past Lk and (causal) past the diagonal get score -inf; returns the
+  // bit mask of the live ones.
+  auto mask_scores = [&](f32x16 (&s)[2], int kv0) -> unsigned {
+    unsigned live = 0u;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * blk + 16 * (r >> 3) + 8 * h + (r & 7);
-          const bool ok = key < Lk && (!CAUSAL || key <= qi + off);
-          live |= (ok ? 1u : 0u) << (16 * blk + r);
-          if (!ok) sacc[blk][r] = -INFINITY;
-        }
-    }
-
-    // ---- running maximum (guide: d_k = max(d_{k-1}, max of chunk k)) ----
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * blk + 16 * (r >> 3) + 8 * h + (r & 7);
+        const bool ok = key < Lk && (!CAUSAL || key <= qi + off);
+        live |= (ok ? 1u : 0u) << (16 * blk + r);
+        if (!ok) s[blk][r] = -INFINITY;
+      }
+    return live;
+  };
+  // Row maximum of a tile in base-2 scaled units (-inf if no live key).
+  auto row_max = [&](const f32x16 (&s)[2]) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
     mx = halves_max(mx);
-    const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
-    // The reference d moves to the new maximum only when the tile's maximum
-    // exceeds it by more than kTau (base 2); then O~ and s are corrected by
-    // exp(d_old - d_new) as in the guide.  Otherwise d stays, the weights
-    // exp(a - d) are at most 2^kTau, and O~ / s is unchanged in real
-    // arithmetic (the correction holds for any reference).  The check is per
-    // row; the branch is taken by the whole wave if any row needs it.
+    return (mx == -INFINITY) ? -INFINITY : mx * c;
+  };
+  // The guide's running maximum d_k = max(d_{k-1}, max of chunk k), with a
+  // lag: the reference d moves to the new maximum only when a tile's
+  // maximum exceeds it by more than kTau (base 2); then O~ and s get the
+  // correction exp(d_old - d_new).  Otherwise d stays, the weights
+  // exp(a - d) are at most 2^kTau, and O~ / s is unchanged in real
+  // arithmetic (the correction holds for any reference).  The branch is
+  // taken by the whole wave if any of its rows needs it.
+  auto advance_max = [&](float m_tile) {
     const bool grow = m_tile > m_ref + kTau;
     if (__any(grow)) {
       const float m_new = grow ? m_tile : m_ref;
@@ -313,29 +334,30 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
     }
+  };
+  // P = exp(a - d), rounded to the MFMA type for the value product; the
+  // denominator sums the fp32 weights (exact LSE).
+  auto probs = [&](const f32x16 (&s)[2], s16x8 (&pb)[4], unsigned live, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-    // ---- P = exp(a - d): fp32 into the denominator, rounded for the MFMA ----
-    s16x8 pb[4];
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int blk = st >> 1, r = 8 * (st & 1) + e;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][r], c, -m_use));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_use));
         if constexpr (MASK) p = ((live >> (16 * blk + r)) & 1u) ? p : 0.f;
         pb[st][e] = (short)round16<BF16>(p);
-        psum += p;  // the denominator keeps fp32 weights (exact LSE)
+        psum += p;
       }
     }
     l_run += psum;
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- O^T += V_j^T P^T; V^T fragments via transposed LDS reads ----
+  };
+  // O^T += V^T P^T; V^T fragments via transposed LDS reads.
+  auto pv = [&](const s16x8 (&pb)[4], const char* Vs) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      if (st) __builtin_amdgcn_sched_barrier(0);
       s16x8 vf[T::DBLK];
 #pragma unroll
       for (int db = 0; db < T::DBLK; ++db) {
@@ -350,47 +372,100 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     }
   };
 
-  // Tiles [0, j_mask) of this wave hold no masked key; tiles from j_mask on
-  // (the causal diagonal band of the wave's rows, the Lk tail) do.  Two
-  // loops instead of a per-tile choice keep the accumulators in one set of
-  // registers.  Every wave runs nkv steps, so barriers stay matched.
-  int j_mask = nkv;
-  if (CAUSAL) {
-    // first tile whose last key lies past the diagonal of the wave's first row
-    const int first_bad = wq0 + off - BN + 2;
-    j_mask = first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN;
-  }
-  if (Lk % BN) j_mask = min(j_mask, Lk / BN);
-  j_mask = __builtin_amdgcn_readfirstlane(min(j_mask, nkv));
-
-  dma(stage0, 0);
-  land(stage0, 0);
+  // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 ----
+  dma_k(kb0, 0);
+  dma_v(vb0, 0);
+  if (nkv > 1) dma_k(kb1, BN);
+  land(vb0, 0);
   __syncthreads();
-  // One pipeline step per tile j: start the DMA of tile j+1 into the other
-  // stage, compute tile j, wait for the DMA, then one workgroup barrier.
-  int j = 0;
-  for (; j < j_mask; ++j) {
-    char* cur = (j & 1) ? stage1 : stage0;
-    char* nxt = (j & 1) ? stage0 : stage1;
-    const int kv0 = j * BN;
-    if (j + 1 < nkv) dma(nxt, kv0 + BN);
-    if (wave_live) tile(cur, cur + T::KBYTES, kv0, std::integral_constant<bool, false>{});
-    if (j + 1 < nkv) land(nxt, kv0 + BN);
-    __syncthreads();
+  f32x16 sa[2], sb[2];
+  unsigned live_a = 0xffffffffu, live_b = 0xffffffffu;
+  if (w_nkv > 0) {
+    scores(sa, kb0);
+    if (j_mask == 0) live_a = mask_scores(sa, 0);
+    advance_max(row_max(sa));
   }
-  for (; j < nkv; ++j) {
-    char* cur = (j & 1) ? stage1 : stage0;
-    char* nxt = (j & 1) ? stage0 : stage1;
-    const int kv0 = j * BN;
-    if (j + 1 < nkv) dma(nxt, kv0 + BN);
-    if (wave_live && kv0 < w_key_end) tile(cur, cur + T::KBYTES, kv0, std::integral_constant<bool, true>{});
-    if (j + 1 < nkv) land(nxt, kv0 + BN);
+  __syncthreads();  // kb0 is refilled with K_2 in step 0
+
+  // ---- step j: holds the scores of tile j (sc), computes those of tile j+1 (sn) ----
+  //   phase A: S_{j+1} = K_{j+1} Q^T on MFMA, overlapped with P_j on VALU
+  //   phase B: O += V_j^T P_j on MFMA, overlapped with the max of S_{j+1}
+  //   then the running-maximum update for tile j+1 (rarely taken branch).
+  // FAST: tiles j and j+1 both computed by this wave and unmasked.
+  // PAR: the parity of j, when the caller knows it at compile time (0 or 1),
+  // otherwise -1; with a known parity every LDS buffer is a fixed array.
+  auto step = [&](int j, f32x16 (&sc)[2], unsigned live_c, f32x16 (&sn)[2], unsigned& live_n,
+                  auto fast_tag, auto par_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    constexpr int PAR = decltype(par_tag)::value;
+    const bool odd = PAR < 0 ? (j & 1) != 0 : PAR == 1;
+    char* kn = odd ? kb0 : kb1;   // K_{j+1}
+    char* vc = odd ? vb1 : vb0;   // V_j
+    char* kf = odd ? kb1 : kb0;   // receives K_{j+2}
+    char* vf = odd ? vb0 : vb1;   // receives V_{j+1}
+    if (j + 2 < nkv) dma_k(kf, (j + 2) * BN);
+    if (j + 1 < nkv) dma_v(vf, (j + 1) * BN);
+    const bool do_cur = FAST || j < w_nkv;
+    const bool do_next = FAST || j + 1 < w_nkv;
+    s16x8 pb[4];
+    float m_next = -INFINITY;
+    if constexpr (FAST) {
+      scores(sn, kn);
+      probs(sc, pb, live_c, std::integral_constant<bool, false>{});
+      // Interleave: LDS fragment reads run PF MFMAs ahead of their use, and
+      // each MFMA is followed by a share of the softmax VALU work.
+      constexpr int PFK = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, PFK, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + PFK < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pv(pb, vc);
+      m_next = row_max(sn);
+      constexpr int PFV = 6;  // transposed reads (two per MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, PFV, 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (2 * i + PFV < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (do_next) scores(sn, kn);
+      if (do_cur) probs(sc, pb, live_c, std::integral_constant<bool, true>{});
+      if (do_cur) pv(pb, vc);
+      if (do_next) {
+        live_n = mask_scores(sn, (j + 1) * BN);
+        m_next = row_max(sn);
+      }
+    }
+    if (do_next) advance_max(m_next);
+    if (j + 1 < nkv) land(vf, (j + 1) * BN);
     __syncthreads();
+  };
+
+  int j = 0;
+  for (; j + 2 < j_mask; j += 2) {
+    step(j, sa, 0xffffffffu, sb, live_b, std::integral_constant<bool, true>{},
+         std::integral_constant<int, 0>{});
+    step(j + 1, sb, 0xffffffffu, sa, live_a, std::integral_constant<bool, true>{},
+         std::integral_constant<int, 1>{});
+  }
+  if (j > 0) live_a = 0xffffffffu;  // tile j < j_mask: no masked key
+  for (; j < nkv; ++j) {
+    step(j, sa, live_a, sb, live_b, std::integral_constant<bool, false>{}, std::integral_constant<int, -1>{});
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) sa[blk] = sb[blk];
+    live_a = live_b;
   }
 
   // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
   const float l_tot = halves_sum(l_run);
-  if (wave_live && qi < Lq) {
+  if (qi < Lq) {
     const float inv = 1.f / l_tot;
     unsigned short* Oq = O + (size_t)bh * Lq * D + (size_t)qi * D;
 #pragma unroll
