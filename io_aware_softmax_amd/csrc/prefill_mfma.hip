@@ -162,15 +162,16 @@ __device__ __forceinline__ void dma16(const char* src_base, unsigned voff, char*
       : "memory", "m0");
 }
 
-// Issue this wave's DMA instructions for one tile of one tensor.
-template <int D, int INST, int PER_WAVE>
+// Issue this wave's DMA instructions for one tile of one tensor.  FULL: the
+// tile lies entirely before Lk (no row needs clamping).
+template <int D, int INST, int PER_WAVE, bool FULL>
 __device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, const unsigned* src_off,
-                                         int w, bool full, int rows_left) {
+                                         int w, int rows_left) {
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int inst = i * NW + w;
     if (inst < INST) {
-      const unsigned o = full ? src_off[i] : dma_clamp<D>(src_off[i], rows_left);
+      const unsigned o = FULL ? src_off[i] : dma_clamp<D>(src_off[i], rows_left);
       dma16(src_tile, o, dst_tile + inst * 1024);
     }
   }
@@ -246,12 +247,22 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   for (int i = 0; i < T::KI; ++i) k_src[i] = dma_src_offset<D>(i * NW + w, lane, T::KSPR);
 #pragma unroll
   for (int i = 0; i < T::VI; ++i) v_src[i] = dma_src_offset<D>(i * NW + w, lane, T::VSPR);
-  auto dma_k = [&](char* buf, int kv0) {
-    dma_tile<D, T::KINST, T::KI>(Kb + (size_t)kv0 * (D * 2), buf, k_src, w, kv0 + BN <= Lk, Lk - kv0);
+  // full_tag: the caller knows the tile lies entirely before Lk.
+  auto dma_k = [&](char* buf, int kv0, auto full_tag) {
+    const char* src = Kb + (size_t)kv0 * (D * 2);
+    if (decltype(full_tag)::value || kv0 + BN <= Lk)
+      dma_tile<D, T::KINST, T::KI, true>(src, buf, k_src, w, Lk - kv0);
+    else
+      dma_tile<D, T::KINST, T::KI, false>(src, buf, k_src, w, Lk - kv0);
   };
-  auto dma_v = [&](char* buf, int kv0) {
-    dma_tile<D, T::VINST, T::VI>(Vb + (size_t)kv0 * (D * 2), buf, v_src, w, kv0 + BN <= Lk, Lk - kv0);
+  auto dma_v = [&](char* buf, int kv0, auto full_tag) {
+    const char* src = Vb + (size_t)kv0 * (D * 2);
+    if (decltype(full_tag)::value || kv0 + BN <= Lk)
+      dma_tile<D, T::VINST, T::VI, true>(src, buf, v_src, w, Lk - kv0);
+    else
+      dma_tile<D, T::VINST, T::VI, false>(src, buf, v_src, w, Lk - kv0);
   };
+  const std::integral_constant<bool, false> maybe_ragged{};
   auto land = [&](char* vbuf, int kv0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (kv0 + BN > Lk) {
@@ -373,9 +384,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   };
 
   // ---- prologue: K_0, V_0, K_1 in LDS; scores of tile 0 ----
-  dma_k(kb0, 0);
-  dma_v(vb0, 0);
-  if (nkv > 1) dma_k(kb1, BN);
+  dma_k(kb0, 0, maybe_ragged);
+  dma_v(vb0, 0, maybe_ragged);
+  if (nkv > 1) dma_k(kb1, BN, maybe_ragged);
   land(vb0, 0);
   __syncthreads();
   f32x16 sa[2], sb[2];
@@ -403,8 +414,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     char* vc = odd ? vb1 : vb0;   // V_j
     char* kf = odd ? kb1 : kb0;   // receives K_{j+2}
     char* vf = odd ? vb0 : vb1;   // receives V_{j+1}
-    if (j + 2 < nkv) dma_k(kf, (j + 2) * BN);
-    if (j + 1 < nkv) dma_v(vf, (j + 1) * BN);
+    // In FAST steps tiles j+1 and j+2 < j_mask <= Lk / BN are whole.
+    if (j + 2 < nkv) dma_k(kf, (j + 2) * BN, std::integral_constant<bool, false>{});
+    if (j + 1 < nkv) dma_v(vf, (j + 1) * BN, fast_tag);
     const bool do_cur = FAST || j < w_nkv;
     const bool do_next = FAST || j + 1 < w_nkv;
     s16x8 pb[4];
