@@ -177,6 +177,116 @@ __device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, c
   }
 }
 
+
+// ---- steady-state step as a fixed sequence of MFMA slots ----
+// One step of a wave computes S_{j+1} = K_{j+1} Q^T (NS MFMAs), the weights
+// P_j of the scores it already holds (VALU), O~ += V_j^T P_j (NP MFMAs) and
+// the row maximum of S_{j+1} (VALU).  The order is fixed in source: slot i
+// issues one MFMA, the LDS read of the operand PF slots ahead (K fragments,
+// then V fragments, so V reads overlap the end of the S products), a share
+// of the softmax elements, a share of the max reduction and now and then one
+// of this wave's DMA instructions for the next tiles, and a scheduling fence
+// keeps the slots apart.  A few softmax elements run before slot 0 so that the
+// first K reads are in flight while the VALU works.
+template <int D>
+struct Slots {
+  using T = Tile<D>;
+  static constexpr int NS = 2 * T::KSTEPS;   // S MFMAs
+  static constexpr int NP = 4 * T::DBLK;     // P V MFMAs
+  static constexpr int N = NS + NP;
+  static constexpr int PF = 4;               // read lookahead, in slots
+  static constexpr int F = 6;                // softmax elements before slot 0
+  static constexpr int NV = NS + 2 * T::DBLK;  // slots the other elements spread over
+  static constexpr int KU = T::KINST / NW;   // K DMA instructions every wave issues
+  static constexpr int KX = T::KINST % NW;   // waves w < KX issue one more, up front
+  static constexpr int VU = T::VINST / NW;
+  static constexpr int NQ = KU + VU;
+  // Slot of softmax element e >= F, of max step m (values 2m, 2m+1), of DMA q.
+  static constexpr int elem_slot(int e) { return (e - F) * NV / (32 - F); }
+  static constexpr int max_slot(int m) { return NS + 2 + m * (NP - 2) / 16; }
+  static constexpr int dma_slot(int q) { return 1 + q * (N - 2) / NQ; }
+  static constexpr bool deadlines_met() {
+    // P_j rows of k-step st feed PV slot NS + st * DBLK.
+    for (int st = 0; st < 4; ++st)
+      if (8 * st + 7 >= F && elem_slot(8 * st + 7) >= NS + st * T::DBLK) return false;
+    return true;
+  }
+  static_assert(deadlines_met(), "softmax element scheduled after its value product");
+  static_assert(T::VINST % NW == 0, "V DMA instructions split evenly over the waves");
+  static_assert(max_slot(15) < N && dma_slot(NQ - 1) < N, "slot overflow");
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ void fast_step(const char* kp, const char* vp, const s16x8 (&qreg)[D / 16],
+                                          const f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&oacc)[D / 32],
+                                          float c, float neg_m, float& psum_out, float& mx_out,
+                                          const char* ksrc, char* kdst, const unsigned* k_off,
+                                          const char* vsrc, char* vdst, const unsigned* v_off, int w) {
+  using T = Tile<D>;
+  using S = Slots<D>;
+  if constexpr (S::KX != 0) {
+    if (w < S::KX) dma16(ksrc, k_off[S::KU], kdst + (S::KU * NW + w) * 1024);
+  }
+  s16x8 fr[S::N];
+  s16x8 pb[4];
+  float psum = 0.f;
+  float mx = -INFINITY;
+  auto read = [&](int r) {
+    if (r < S::NS) {
+      fr[r] = *reinterpret_cast<const s16x8*>(kp + 32 * (r & 1) * T::KPITCH + 32 * (r >> 1));
+    } else {
+      const int x = r - S::NS, st = x / T::DBLK, db = x % T::DBLK;
+      const char* p = vp + 16 * st * T::VPITCH + 64 * db;
+      const s16x4 lo = lds_read_tr(p);
+      const s16x4 hi = lds_read_tr(p + 4 * T::VPITCH);
+      fr[r] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  auto elem = [&](int e) {
+    const int blk = e >> 4, r = e & 15;
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
+    pb[e >> 3][e & 7] = (short)round16<BF16>(p);
+    psum += p;
+  };
+#pragma unroll
+  for (int r = 0; r < S::PF; ++r) read(r);
+#pragma unroll
+  for (int e = 0; e < S::F; ++e) elem(e);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < S::N; ++i) {
+    if (i + S::PF < S::N) read(i + S::PF);
+#pragma unroll
+    for (int q = 0; q < S::NQ; ++q) {
+      if (S::dma_slot(q) == i) {
+        if (q < S::KU)
+          dma16(ksrc, k_off[q], kdst + (q * NW + w) * 1024);
+        else
+          dma16(vsrc, v_off[q - S::KU], vdst + ((q - S::KU) * NW + w) * 1024);
+      }
+    }
+    if (i < S::NS) {
+      const int blk = i & 1;
+      sn[blk] = mfma32<BF16>(fr[i], qreg[i >> 1], i < 2 ? f32x16{} : sn[blk]);
+    } else {
+      const int x = i - S::NS;
+      oacc[x % T::DBLK] = mfma32<BF16>(fr[i], pb[x / T::DBLK], oacc[x % T::DBLK]);
+    }
+#pragma unroll
+    for (int e = S::F; e < 32; ++e)
+      if (S::elem_slot(e) == i) elem(e);
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      if (S::max_slot(m) == i) {
+        mx = fmaxf(mx, sn[m >> 3][2 * (m & 7)]);
+        mx = fmaxf(mx, sn[m >> 3][2 * (m & 7) + 1]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  psum_out = psum;
+  mx_out = mx;
+}
+
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
@@ -415,37 +525,24 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     char* kf = odd ? kb1 : kb0;   // receives K_{j+2}
     char* vf = odd ? vb0 : vb1;   // receives V_{j+1}
     // In FAST steps tiles j+1 and j+2 < j_mask <= Lk / BN are whole.
-    if (j + 2 < nkv) dma_k(kf, (j + 2) * BN, std::integral_constant<bool, false>{});
-    if (j + 1 < nkv) dma_v(vf, (j + 1) * BN, fast_tag);
+    if constexpr (!FAST) {
+      if (j + 2 < nkv) dma_k(kf, (j + 2) * BN, std::integral_constant<bool, false>{});
+      if (j + 1 < nkv) dma_v(vf, (j + 1) * BN, fast_tag);
+    }
     const bool do_cur = FAST || j < w_nkv;
     const bool do_next = FAST || j + 1 < w_nkv;
     s16x8 pb[4];
     float m_next = -INFINITY;
     if constexpr (FAST) {
-      scores(sn, kn);
-      probs(sc, pb, live_c, std::integral_constant<bool, false>{});
-      // Interleave: LDS fragment reads run PF MFMAs ahead of their use, and
-      // each MFMA is followed by a share of the softmax VALU work.
-      constexpr int PFK = 4;
-      __builtin_amdgcn_sched_group_barrier(0x100, PFK, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + PFK < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      pv(pb, vc);
-      m_next = row_max(sn);
-      constexpr int PFV = 6;  // transposed reads (two per MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, PFV, 1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (2 * i + PFV < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float psum, mx;
+      fast_step<BF16, D>(kn + prow * T::KPITCH + 16 * h,
+                         vc + (8 * h + (li >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (li & 3)) * 2, qreg, sc,
+                         sn, oacc, c, -m_use, psum, mx, Kb + (size_t)(j + 2) * BN * (D * 2), kf, k_src,
+                         Vb + (size_t)(j + 1) * BN * (D * 2), vf, v_src, w);
+      l_run += psum;
+      mx = halves_max(mx);
+      m_next = (mx == -INFINITY) ? -INFINITY : mx * c;
     } else {
       if (do_next) scores(sn, kn);
       if (do_cur) probs(sc, pb, live_c, std::integral_constant<bool, true>{});
@@ -460,8 +557,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     __syncthreads();
   };
 
+  // Fast steps j also need K_{j+2} to exist and be whole (its DMA is issued
+  // unclamped inside the step).
+  const int k_whole_end = min(nkv, Lk / BN);
   int j = 0;
-  for (; j + 2 < j_mask; j += 2) {
+  for (; j + 2 < j_mask && j + 3 < k_whole_end; j += 2) {
     step(j, sa, 0xffffffffu, sb, live_b, std::integral_constant<bool, true>{},
          std::integral_constant<int, 0>{});
     step(j + 1, sb, 0xffffffffu, sa, live_a, std::integral_constant<bool, true>{},
