@@ -40,8 +40,10 @@ DECODE = "decode_bf16_32k"
 def _parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    # The GPU's clocks take a few tens of milliseconds of sustained load to
+    # settle; the default warm-up (about 100 ms) reaches that state first.
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--splits", type=int, default=0, help="decode split count (0 = library choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=24, help="heads of the prefill workload the oracle times")

@@ -123,13 +123,76 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
 // K/V tiles go HBM -> LDS by DMA (global_load_lds_dwordx4): one instruction
 // moves 64 lanes x 16 B into 1 KB of consecutive LDS, here a run of 16-byte
 // slots of the padded tile.  Lane l of DMA instruction i fills slot 64 i + l
-// (row = slot / slots-per-row, chunk = the rest); pad slots fetch chunk 0 of
-// their row again (in bounds, never read).  Wave w issues instructions w,
-// w + 4, ...
+// (row = slot / slots-per-row, chunk = the rest).
 //
+// One global_load_lds_dwordx4 moves 16 bytes per lane from global memory to
+// LDS at M0 + 16 * lane; its immediate offset is added to BOTH addresses.
+// A wave issues a run of up to four instructions of consecutive LDS
+// kilobytes under one M0 value with offsets 0, 1024, 2048, 3072; the global
+// base passed in SGPRs is lowered by kDmaBias so that every per-lane offset
+// (source offset + kDmaBias - offset of the instruction in its run) stays
+// non-negative.  Written as inline assembly so that the compiler's LGKM wait
+// model does not count the DMA: with the builtin, every wait for an LDS read
+// becomes a wait for all outstanding LDS traffic including this DMA.
+// Completion is awaited explicitly with s_waitcnt vmcnt(0).
+constexpr unsigned kDmaBias = 4096u;
+
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+template <int G>
+__device__ __forceinline__ void dma_run(const char* gbase, const unsigned* voff, unsigned m0) {
+  static_assert(G >= 1 && G <= 4, "one M0 run holds 1 to 4 instructions");
+  if constexpr (G == 1)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n"
+                 : : "s"(gbase), "s"(m0), "v"(voff[0]) : "memory", "m0");
+  else if constexpr (G == 2)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n\t"
+                 "global_load_lds_dwordx4 %3, %0 offset:1024\n"
+                 : : "s"(gbase), "s"(m0), "v"(voff[0]), "v"(voff[1]) : "memory", "m0");
+  else if constexpr (G == 3)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n\t"
+                 "global_load_lds_dwordx4 %3, %0 offset:1024\n\tglobal_load_lds_dwordx4 %4, %0 offset:2048\n"
+                 : : "s"(gbase), "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n\t"
+                 "global_load_lds_dwordx4 %3, %0 offset:1024\n\tglobal_load_lds_dwordx4 %4, %0 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %5, %0 offset:3072\n"
+                 : : "s"(gbase), "s"(m0), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3])
+                 : "memory", "m0");
+}
+
+// Run of g instructions, g known once loops are unrolled.
+__device__ __forceinline__ void dma_run_n(int g, const char* gbase, const unsigned* voff, unsigned m0) {
+  switch (g) {
+    case 1: dma_run<1>(gbase, voff, m0); break;
+    case 2: dma_run<2>(gbase, voff, m0); break;
+    case 3: dma_run<3>(gbase, voff, m0); break;
+    default: dma_run<4>(gbase, voff, m0); break;
+  }
+}
+
+// Per-wave DMA plan of one tile with INST instructions: wave w issues the
+// U = INST / NW instructions w U .. w U + U - 1 (consecutive LDS kilobytes),
+// in runs of at most RUN, and, when INST % NW != 0, waves w < INST % NW issue
+// instruction U NW + w as a run of one.  Index i of a wave's list:
+// i < U: instruction w U + i; i == U: the extra one.
+template <int INST, int RUN>
+struct DmaPlan {
+  static constexpr int U = INST / NW;
+  static constexpr int X = INST % NW;
+  static constexpr int N = U + (X ? 1 : 0);  // list length (the extra may be idle)
+  static constexpr int RUNS = (U + RUN - 1) / RUN;
+  static constexpr int run_first(int r) { return r * RUN; }
+  static constexpr int run_len(int r) { return (r + 1) * RUN <= U ? RUN : U - r * RUN; }
+  static constexpr int pos_in_run(int i) { return i < U ? i % RUN : 0; }
+  __device__ static int inst(int i, int w) { return i < U ? w * U + i : U * NW + w; }
+};
+
 // Byte offset, within one tile of the source tensor, of the chunk that lane
 // `lane` fetches for DMA instruction `inst` of a tile with `spr` slots per
-// row.
+// row; pad slots fetch chunk 0 of their row again (in bounds, never read).
 template <int D>
 __device__ __forceinline__ unsigned dma_src_offset(int inst, int lane, int spr) {
   const int slot = inst * 64 + lane;
@@ -138,73 +201,66 @@ __device__ __forceinline__ unsigned dma_src_offset(int inst, int lane, int spr) 
   return (unsigned)row * (D * 2) + (unsigned)(chunk < D / 8 ? chunk : 0) * 16;
 }
 
-// Rows at or past `rows_left` (keys past Lk) are redirected to row
-// rows_left - 1 of the tile, which is in bounds.
-template <int D>
-__device__ __forceinline__ unsigned dma_clamp(unsigned off, int rows_left) {
-  const int row = (int)(off / (D * 2));
-  return row < rows_left ? off : (unsigned)(rows_left - 1) * (D * 2) + off % (D * 2);
-}
-
-// One global_load_lds_dwordx4: 16 bytes per lane from src_base + voff into
-// LDS at lds_base + 16 * lane.  Written as inline assembly so that the
-// compiler's LGKM wait model does not count it: with the builtin, every wait
-// for an LDS read becomes a wait for all outstanding LDS traffic including
-// this DMA.  Completion is awaited explicitly with s_waitcnt vmcnt(0).
-__device__ __forceinline__ void dma16(const char* src_base, unsigned voff, char* lds_base) {
-  const unsigned lds = (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds_base;
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1\n"
-      :
-      : "v"(voff), "s"(src_base), "s"(lds)
-      : "memory", "m0");
-}
-
-// Issue this wave's DMA instructions for one tile of one tensor.  FULL: the
-// tile lies entirely before Lk (no row needs clamping).
-template <int D, int INST, int PER_WAVE, bool FULL>
-__device__ __forceinline__ void dma_tile(const char* src_tile, char* dst_tile, const unsigned* src_off,
-                                         int w, int rows_left) {
+// Issue a wave's DMA for one whole tile (every row before Lk).  voff holds
+// the biased per-lane offsets of the wave's list; gbase = tile - kDmaBias.
+template <int INST, int RUN>
+__device__ __forceinline__ void dma_tile_whole(const char* gbase, char* dst, const unsigned* voff, int w) {
+  using P = DmaPlan<INST, RUN>;
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = i * NW + w;
-    if (inst < INST) {
-      const unsigned o = FULL ? src_off[i] : dma_clamp<D>(src_off[i], rows_left);
-      dma16(src_tile, o, dst_tile + inst * 1024);
-    }
+  for (int r = 0; r < P::RUNS; ++r)
+    dma_run_n(P::run_len(r), gbase, voff + P::run_first(r), lds_addr(dst + P::inst(P::run_first(r), w) * 1024));
+  if constexpr (P::X != 0) {
+    if (w < P::X) dma_run<1>(gbase, voff + P::U, lds_addr(dst + P::inst(P::U, w) * 1024));
   }
 }
 
+// Ragged tile: rows at or past `rows_left` read row rows_left - 1 instead
+// (in bounds); one instruction per run.
+template <int D, int INST, int RUN>
+__device__ __forceinline__ void dma_tile_ragged(const char* gbase, char* dst, const unsigned* voff, int w,
+                                                int rows_left) {
+  using P = DmaPlan<INST, RUN>;
+#pragma unroll
+  for (int i = 0; i < P::N; ++i) {
+    if (i < P::U || w < P::X) {
+      const unsigned off = voff[i] - (kDmaBias - P::pos_in_run(i) * 1024u);
+      const int row = (int)(off / (D * 2));
+      const unsigned o = row < rows_left ? off : (unsigned)(rows_left - 1) * (D * 2) + off % (D * 2);
+      const unsigned vo = o + kDmaBias;
+      dma_run<1>(gbase, &vo, lds_addr(dst + P::inst(i, w) * 1024));
+    }
+  }
+}
 
 // ---- steady-state step as a fixed sequence of MFMA slots ----
 // One step of a wave computes S_{j+1} = K_{j+1} Q^T (NS MFMAs), the weights
 // P_j of the scores it already holds (VALU), O~ += V_j^T P_j (NP MFMAs) and
 // the row maximum of S_{j+1} (VALU).  The order is fixed in source: slot i
-// issues one MFMA, the LDS read of the operand PF slots ahead (K fragments,
-// then V fragments, so V reads overlap the end of the S products), a share
-// of the softmax elements, a share of the max reduction and now and then one
-// of this wave's DMA instructions for the next tiles, and a scheduling fence
-// keeps the slots apart.  A few softmax elements run before slot 0 so that the
-// first K reads are in flight while the VALU works.
+// issues one MFMA, a share of the softmax elements, a share of the max
+// reduction and now and then one DMA run for the next tiles; every even slot
+// issues the LDS reads of the operand pair PF slots ahead (K fragments, then
+// V fragments, so V reads overlap the end of the S products), the later
+// operand first, so that a single wait covers both MFMAs of the pair.  A
+// scheduling fence keeps the slots apart.  A few softmax elements run before
+// slot 0 so that the first K reads are in flight while the VALU works.
+constexpr int kDmaRun = 2;  // DMA instructions per M0 run
+
 template <int D>
 struct Slots {
   using T = Tile<D>;
+  using KP = DmaPlan<T::KINST, kDmaRun>;
+  using VP = DmaPlan<T::VINST, kDmaRun>;
   static constexpr int NS = 2 * T::KSTEPS;   // S MFMAs
   static constexpr int NP = 4 * T::DBLK;     // P V MFMAs
   static constexpr int N = NS + NP;
-  static constexpr int PF = 4;               // read lookahead, in slots
+  static constexpr int PF = 4;               // read lookahead, in slots (even)
   static constexpr int F = 6;                // softmax elements before slot 0
   static constexpr int NV = NS + 2 * T::DBLK;  // slots the other elements spread over
-  static constexpr int KU = T::KINST / NW;   // K DMA instructions every wave issues
-  static constexpr int KX = T::KINST % NW;   // waves w < KX issue one more, up front
-  static constexpr int VU = T::VINST / NW;
-  static constexpr int NQ = KU + VU;
-  // Slot of softmax element e >= F, of max step m (values 2m, 2m+1), of DMA q.
+  static constexpr int NR = KP::RUNS + VP::RUNS;  // DMA runs per step (K first)
+  // Slot of softmax element e >= F, of max step m (values 2m, 2m+1), of DMA run q.
   static constexpr int elem_slot(int e) { return (e - F) * NV / (32 - F); }
   static constexpr int max_slot(int m) { return NS + 2 + m * (NP - 2) / 16; }
-  static constexpr int dma_slot(int q) { return 1 + q * (N - 2) / NQ; }
+  static constexpr int dma_slot(int q) { return 1 + q * (N - 2) / NR; }
   static constexpr bool deadlines_met() {
     // P_j rows of k-step st feed PV slot NS + st * DBLK.
     for (int st = 0; st < 4; ++st)
@@ -212,20 +268,25 @@ struct Slots {
     return true;
   }
   static_assert(deadlines_met(), "softmax element scheduled after its value product");
-  static_assert(T::VINST % NW == 0, "V DMA instructions split evenly over the waves");
-  static_assert(max_slot(15) < N && dma_slot(NQ - 1) < N, "slot overflow");
+  static_assert(PF % 2 == 0 && NS % 2 == 0 && NP % 2 == 0, "operand pairs");
+  static_assert(max_slot(15) < N && dma_slot(NR - 1) < N, "slot overflow");
 };
 
 template <bool BF16, int D>
 __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const s16x8 (&qreg)[D / 16],
                                           const f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&oacc)[D / 32],
                                           float c, float neg_m, float& psum_out, float& mx_out,
-                                          const char* ksrc, char* kdst, const unsigned* k_off,
-                                          const char* vsrc, char* vdst, const unsigned* v_off, int w) {
+                                          const char* kgbase, char* kdst, const unsigned* k_off,
+                                          const char* vgbase, char* vdst, const unsigned* v_off, int w) {
   using T = Tile<D>;
   using S = Slots<D>;
-  if constexpr (S::KX != 0) {
-    if (w < S::KX) dma16(ksrc, k_off[S::KU], kdst + (S::KU * NW + w) * 1024);
+  using KP = typename S::KP;
+  using VP = typename S::VP;
+  if constexpr (VP::X != 0) {
+    if (w < VP::X) dma_run<1>(vgbase, v_off + VP::U, lds_addr(vdst + VP::inst(VP::U, w) * 1024));
+  }
+  if constexpr (KP::X != 0) {
+    if (w < KP::X) dma_run<1>(kgbase, k_off + KP::U, lds_addr(kdst + KP::inst(KP::U, w) * 1024));
   }
   s16x8 fr[S::N];
   s16x8 pb[4];
@@ -242,29 +303,37 @@ __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const 
       fr[r] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
+  auto read_pair = [&](int r) {  // operands r and r + 1, the later one first
+    read(r + 1);
+    read(r);
+  };
   auto elem = [&](int e) {
     const int blk = e >> 4, r = e & 15;
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
     pb[e >> 3][e & 7] = (short)round16<BF16>(p);
     psum += p;
   };
+  auto dma = [&](int q) {
+    if (q < KP::RUNS) {
+      const int i0 = KP::run_first(q);
+      dma_run_n(KP::run_len(q), kgbase, k_off + i0, lds_addr(kdst + KP::inst(i0, w) * 1024));
+    } else {
+      const int qv = q - KP::RUNS;
+      const int i0 = VP::run_first(qv);
+      dma_run_n(VP::run_len(qv), vgbase, v_off + i0, lds_addr(vdst + VP::inst(i0, w) * 1024));
+    }
+  };
 #pragma unroll
-  for (int r = 0; r < S::PF; ++r) read(r);
+  for (int r = 0; r < S::PF; r += 2) read_pair(r);
 #pragma unroll
   for (int e = 0; e < S::F; ++e) elem(e);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < S::N; ++i) {
-    if (i + S::PF < S::N) read(i + S::PF);
+    if (i % 2 == 0 && i + S::PF < S::N) read_pair(i + S::PF);
 #pragma unroll
-    for (int q = 0; q < S::NQ; ++q) {
-      if (S::dma_slot(q) == i) {
-        if (q < S::KU)
-          dma16(ksrc, k_off[q], kdst + (q * NW + w) * 1024);
-        else
-          dma16(vsrc, v_off[q - S::KU], vdst + ((q - S::KU) * NW + w) * 1024);
-      }
-    }
+    for (int q = 0; q < S::NR; ++q)
+      if (S::dma_slot(q) == i) dma(q);
     if (i < S::NS) {
       const int blk = i & 1;
       sn[blk] = mfma32<BF16>(fr[i], qreg[i >> 1], i < 2 ? f32x16{} : sn[blk]);
@@ -349,39 +418,49 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
 
-  // DMA of one K or V tile (see dma_tile); rows past Lk read row Lk-1 and
-  // the V slots of those rows are zeroed once the DMA has landed.
-  unsigned k_src[T::KI];
-  unsigned v_src[T::VI];
+  // DMA of one K or V tile (DmaPlan); rows past Lk read row Lk-1 and the V
+  // slots of those rows are zeroed once the DMA has landed.  Offsets are
+  // biased for dma_run.
+  using KP = typename Slots<D>::KP;
+  using VP = typename Slots<D>::VP;
+  unsigned k_src[KP::N];
+  unsigned v_src[VP::N];
 #pragma unroll
-  for (int i = 0; i < T::KI; ++i) k_src[i] = dma_src_offset<D>(i * NW + w, lane, T::KSPR);
+  for (int i = 0; i < KP::N; ++i)
+    k_src[i] = dma_src_offset<D>(KP::inst(i, w), lane, T::KSPR) + kDmaBias - KP::pos_in_run(i) * 1024u;
 #pragma unroll
-  for (int i = 0; i < T::VI; ++i) v_src[i] = dma_src_offset<D>(i * NW + w, lane, T::VSPR);
+  for (int i = 0; i < VP::N; ++i)
+    v_src[i] = dma_src_offset<D>(VP::inst(i, w), lane, T::VSPR) + kDmaBias - VP::pos_in_run(i) * 1024u;
+  // Global base of a tile lowered by the DMA bias (the sum with every lane
+  // offset is inside the tile).
+  auto biased = [](const char* p) {
+    return reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) - kDmaBias);
+  };
   // full_tag: the caller knows the tile lies entirely before Lk.
   auto dma_k = [&](char* buf, int kv0, auto full_tag) {
-    const char* src = Kb + (size_t)kv0 * (D * 2);
+    const char* g = biased(Kb + (size_t)kv0 * (D * 2));
     if (decltype(full_tag)::value || kv0 + BN <= Lk)
-      dma_tile<D, T::KINST, T::KI, true>(src, buf, k_src, w, Lk - kv0);
+      dma_tile_whole<T::KINST, kDmaRun>(g, buf, k_src, w);
     else
-      dma_tile<D, T::KINST, T::KI, false>(src, buf, k_src, w, Lk - kv0);
+      dma_tile_ragged<D, T::KINST, kDmaRun>(g, buf, k_src, w, Lk - kv0);
   };
   auto dma_v = [&](char* buf, int kv0, auto full_tag) {
-    const char* src = Vb + (size_t)kv0 * (D * 2);
+    const char* g = biased(Vb + (size_t)kv0 * (D * 2));
     if (decltype(full_tag)::value || kv0 + BN <= Lk)
-      dma_tile<D, T::VINST, T::VI, true>(src, buf, v_src, w, Lk - kv0);
+      dma_tile_whole<T::VINST, kDmaRun>(g, buf, v_src, w);
     else
-      dma_tile<D, T::VINST, T::VI, false>(src, buf, v_src, w, Lk - kv0);
+      dma_tile_ragged<D, T::VINST, kDmaRun>(g, buf, v_src, w, Lk - kv0);
   };
   const std::integral_constant<bool, false> maybe_ragged{};
   auto land = [&](char* vbuf, int kv0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (kv0 + BN > Lk) {
 #pragma unroll
-      for (int i = 0; i < T::VI; ++i) {
-        const int inst = i * NW + w;
-        const int slot = inst * 64 + lane;
-        if (inst < T::VINST && kv0 + slot / T::VSPR >= Lk)
-          *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < VP::N; ++i) {
+        if (i < VP::U || w < VP::X) {
+          const int slot = VP::inst(i, w) * 64 + lane;
+          if (kv0 + slot / T::VSPR >= Lk) *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   };
@@ -538,8 +617,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
       float psum, mx;
       fast_step<BF16, D>(kn + prow * T::KPITCH + 16 * h,
                          vc + (8 * h + (li >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (li & 3)) * 2, qreg, sc,
-                         sn, oacc, c, -m_use, psum, mx, Kb + (size_t)(j + 2) * BN * (D * 2), kf, k_src,
-                         Vb + (size_t)(j + 1) * BN * (D * 2), vf, v_src, w);
+                         sn, oacc, c, -m_use, psum, mx, biased(Kb + (size_t)(j + 2) * BN * (D * 2)), kf, k_src,
+                         biased(Vb + (size_t)(j + 1) * BN * (D * 2)), vf, v_src, w);
       l_run += psum;
       mx = halves_max(mx);
       m_next = (mx == -INFINITY) ? -INFINITY : mx * c;
