@@ -45,6 +45,8 @@ def _parse():
     # settle; the default warm-up (about 100 ms) reaches that state first.
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--splits", type=int, default=0, help="decode split count (0 = library choice)")
+    p.add_argument("--parts", default="prefill,decode",
+                   help="comma-separated parts of the step to run (prefill, decode)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=24, help="heads of the prefill workload the oracle times")
     return p.parse_args()
@@ -121,7 +123,11 @@ def main():
 
     wp = inputs.WORKLOADS[PREFILL]
     wd = inputs.WORKLOADS[DECODE]
-    run_p = run_d = True
+    parts = {x.strip() for x in args.parts.split(",") if x.strip()}
+    if not parts or parts - {"prefill", "decode"}:
+        print("--parts takes prefill and/or decode", file=sys.stderr)
+        sys.exit(2)
+    run_p, run_d = "prefill" in parts, "decode" in parts
 
     t_gen = time.perf_counter()
     if run_p:

@@ -223,7 +223,9 @@ __device__ __forceinline__ void dma_tile_ragged(const char* gbase, char* dst, co
 #pragma unroll
   for (int i = 0; i < P::N; ++i) {
     if (i < P::U || w < P::X) {
-      const unsigned off = voff[i] - (kDmaBias - P::pos_in_run(i) * 1024u);
+      unsigned off = voff[i];
+      asm volatile("" : "+v"(off));  // not hoisted out of the tile loop
+      off -= kDmaBias - P::pos_in_run(i) * 1024u;
       const int row = (int)(off / (D * 2));
       const unsigned o = row < rows_left ? off : (unsigned)(rows_left - 1) * (D * 2) + off % (D * 2);
       const unsigned vo = o + kDmaBias;
@@ -495,13 +497,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   // Keys past Lk and (causal) past the diagonal get score -inf; returns the
   // bit mask of the live ones.
   auto mask_scores = [&](f32x16 (&s)[2], int kv0) -> unsigned {
+    // Per-lane key offset and query made opaque here, so the per-element
+    // bounds are not hoisted out of the tile loop (registers).
+    int hk = 8 * h, q = qi;
+    asm volatile("" : "+v"(hk), "+v"(q));
     unsigned live = 0u;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * blk + 16 * (r >> 3) + 8 * h + (r & 7);
-        const bool ok = key < Lk && (!CAUSAL || key <= qi + off);
+        const int key = kv0 + 32 * blk + 16 * (r >> 3) + hk + (r & 7);
+        const bool ok = key < Lk && (!CAUSAL || key <= q + off);
         live |= (ok ? 1u : 0u) << (16 * blk + r);
         if (!ok) s[blk][r] = -INFINITY;
       }
@@ -623,9 +629,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
       mx = halves_max(mx);
       m_next = (mx == -INFINITY) ? -INFINITY : mx * c;
     } else {
+      // Fences between the phases keep the operand reads of one phase from
+      // being hoisted into the previous one (register pressure).
       if (do_next) scores(sn, kn);
+      __builtin_amdgcn_sched_barrier(0);
       if (do_cur) probs(sc, pb, live_c, std::integral_constant<bool, true>{});
+      __builtin_amdgcn_sched_barrier(0);
       if (do_cur) pv(pb, vc);
+      __builtin_amdgcn_sched_barrier(0);
       if (do_next) {
         live_n = mask_scores(sn, (j + 1) * BN);
         m_next = row_max(sn);
@@ -655,22 +666,34 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   }
 
   // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
+  // O goes through LDS (this wave's 32 rows, padded pitch) so that the
+  // global stores are whole 16-byte chunks of consecutive rows.  Every wave
+  // has passed the last barrier of the loop, so the V buffers are free.
+  constexpr int OPITCH = D * 2 + 16;
+  static_assert(2 * 32 * OPITCH <= T::VBYTES, "two waves' rows of O fit in one V buffer");
+  char* ob = (w < 2 ? vb0 : vb1) + (w & 1) * 32 * OPITCH;
   const float l_tot = halves_sum(l_run);
-  if (qi < Lq) {
-    const float inv = 1.f / l_tot;
-    unsigned short* Oq = O + (size_t)bh * Lq * D + (size_t)qi * D;
+  const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int db = 0; db < T::DBLK; ++db)
+  for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = 32 * db + 8 * jj + 4 * h;
-        const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
-                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
-        const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
-                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(Oq + d) = make_uint2(lo, hi);
-      }
-    if (h == 0) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = 32 * db + 8 * jj + 4 * h;
+      const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
+                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
+      const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
+                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(ob + n * OPITCH + d * 2) = make_uint2(lo, hi);
+    }
+  if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
+  __syncthreads();
+  constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+#pragma unroll
+  for (int i = 0; i < 32 / ROWS; ++i) {
+    const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + chunk * 16);
+    if (wq0 + row < Lq)
+      *reinterpret_cast<u32x4*>(O + ((size_t)bh * Lq + wq0 + row) * D + chunk * 8) = v;
   }
 }
 
