@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "attn.h"
@@ -55,6 +56,16 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
       overlaps(o, nq, lse, nl))
     return ATTN_ERR_ALIAS;
   return ATTN_OK;
+}
+
+// ATTN_PREFILL_KERNEL=single forces the single-group 16-bit prefill kernel
+// everywhere (tests compare the two kernels); read once.
+int prefill_variant() {
+  static const int v = [] {
+    const char* e = std::getenv("ATTN_PREFILL_KERNEL");
+    return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
+  }();
+  return v;
 }
 
 int auto_splits(int64_t BH, int Lk) {
@@ -123,8 +134,16 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
   a.neg = scale < 0.f;
   const int64_t nqt = (int64_t(Lq) + 127) / 128;
   if (int64_t(a.BH) * nqt > kMaxWorkgroups) return ATTN_ERR_DIM;
-  const hipError_t e = dtype == ATTN_F32 ? attn::launch_prefill_f32(D, causal != 0, a, s)
-                                         : attn::launch_prefill_mfma(dtype, D, causal != 0, a, s);
+  // 16-bit inputs at D = 128 with a nonzero scale take the two-group kernel;
+  // D = 64 (softmax-bound: half the products per score) and scale 0 (whose
+  // masked keys need explicit zero weights) take the single-group kernel.
+  hipError_t e;
+  if (dtype == ATTN_F32)
+    e = attn::launch_prefill_f32(D, causal != 0, a, s);
+  else if (D == 128 && a.c > 0.f && prefill_variant() != 1)
+    e = attn::launch_prefill_pp(dtype, causal != 0, a, s);
+  else
+    e = attn::launch_prefill_mfma(dtype, D, causal != 0, a, s);
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -40,8 +40,14 @@ struct DecodeArgs {
   bool neg;
 };
 
+// Workgroups of `kernel` (block threads, static LDS only) that device `dev`
+// holds resident at once: compute units times workgroups per unit.  Cached.
+hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out);
+
 // Tiled one-pass prefill on MFMA for 16-bit inputs (dtype 1 = f16, 2 = bf16).
 hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
+// Two-group (ping-pong) variant of the 16-bit prefill for D = 128.
+hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
 // The same algorithm with fp32 inputs on the fp32 MFMA.
 hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Split-KV decode: partials then combine, both on stream s.

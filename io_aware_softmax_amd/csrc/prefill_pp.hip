@@ -1,0 +1,496 @@
+// Tiled one-pass attention forward (prefill) for fp16 / bf16 at D = 128 on
+// gfx950: two wave groups in opposite phases ("ping-pong").
+//
+// Method: the online softmax of the quidproquo.cc guide "Faster Generation,
+// Part 1: Flash Attention" (section "Mechanism: run with the wrong answer,
+// then correct it", both "Expand" boxes): for each key tile the running row
+// maximum d, running denominator s and output accumulator are corrected by
+// exp(d_old - d_new) before the tile's contribution is added.  The output is
+// kept un-normalised (O~ = s * O) and divided by s once at the end.  Scores,
+// scale, mask, softmax and the value product are fused per tile with no
+// score matrix in device memory (comfyai.app chapter "6.3 FlashAttention",
+// section 6.3.3, "Kernel Fusion" and "Full Forward Process").
+//
+// Work decomposition.  A workgroup of 8 waves owns 256 query rows (32 per
+// wave) of one (batch, head) and streams the key/value tiles of 64 rows once
+// for all of them.  Waves w and w + 4 share a SIMD.  Waves 0-3 (group 0) and
+// 4-7 (group 1) run the same per-tile work half a step apart:
+//   matrix phase   S_{j+1} = K_{j+1} Q^T and O~ += V_j^T P_j^T (32 MFMAs at
+//                  D = 128, operands read from LDS a few MFMAs ahead);
+//   softmax phase  row maximum of S_{j+1}, lazy correction of O~ and s,
+//                  P_{j+1} = exp(a - d) rounded to the MFMA type, s += sum.
+// While one wave of a SIMD is in its matrix phase the other is in its
+// softmax phase, so the MFMA pipe runs one wave's products while the vector
+// ALU runs the other wave's exponentials.  A workgroup barrier separates the
+// half steps; the matrix-phase wave runs at the higher issue priority.
+// Group 1 issues the K/V tile DMA (HBM -> LDS, no VGPR round trip) for the
+// next step during its softmax phase and waits for it at the end of the
+// following half step, so each DMA has a whole step to land.  K/V tiles are
+// double buffered: step j reads K_{j+1} and V_j while K_{j+2} and V_{j+1}
+// land.
+//
+// Register layout (per wave, as in the single-group kernel): Q^T is the B
+// operand of v_mfma_f32_32x32x16; K rows are read with bits 2 and 3 of the
+// row index swapped so that each lane's score registers are already the B
+// operand (P^T, 8 consecutive keys) of the value product; V is read
+// transposed from row-major LDS with ds_read_b64_tr_b16.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "attn_internal.hpp"
+#include "mfma_tile.hpp"
+
+namespace attn {
+namespace {
+
+using namespace mt;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // query rows per workgroup
+constexpr int kRun = 2;             // DMA instructions per M0 run
+constexpr int kDmaWaves = 4;        // group 1 issues the DMA
+// Largest lag (base 2) of the reference maximum behind the true running
+// maximum: weights exp(a - d) stay below 2^8.
+constexpr float kTau = 8.f;
+constexpr float kTauWeight = 256.f;  // 2^kTau
+
+template <int D>
+struct Layout {
+  using T = Tile<D>;
+  static constexpr int K0 = 0;
+  static constexpr int K1 = T::KBYTES;
+  static constexpr int V0 = 2 * T::KBYTES;
+  static constexpr int V1 = 2 * T::KBYTES + T::VBYTES;
+  static constexpr int TOTAL = 2 * (T::KBYTES + T::VBYTES);
+  static constexpr int OPITCH = D * 2 + 16;  // staging pitch of O rows
+  static_assert(kWaves * 32 * OPITCH <= TOTAL, "every wave's O rows fit in the tile buffers");
+};
+
+// Workgroup barrier that does not wait for outstanding vector-memory loads
+// (the DMA in flight), only for this wave's LDS and scalar traffic.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Matrix phase of one wave: S = K_{j+1} Q^T (DO_S) and O~ += V_j^T P_j^T
+// (DO_PV), one MFMA per slot, each operand read PF slots ahead.  hook(i)
+// runs at the start of slot i (the DMA issue of the next tiles rides here:
+// the wave waits for the MFMA pipe anyway, so a stalled DMA issue costs
+// little).
+template <bool BF16, int D, bool DO_S, bool DO_PV, class Hook>
+__device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbase, const s16x8 (&qreg)[D / 16],
+                                             f32x16 (&s)[2], const s16x8 (&pb)[4], f32x16 (&oacc)[D / 32],
+                                             Hook&& hook) {
+  using T = Tile<D>;
+  constexpr int NS = DO_S ? 2 * T::KSTEPS : 0;
+  constexpr int NP = DO_PV ? 4 * T::DBLK : 0;
+  constexpr int N = NS + NP;
+  constexpr int PF = 6;
+  s16x8 fr[N];
+  auto read = [&](int r) __attribute__((always_inline)) {
+    if (r < NS) {
+      fr[r] = *reinterpret_cast<const s16x8*>(kbase + 32 * (r & 1) * T::KPITCH + 32 * (r >> 1));
+    } else {
+      const int x = r - NS, st = x / T::DBLK, db = x % T::DBLK;
+      const char* p = vbase + 16 * st * T::VPITCH + 64 * db;
+      const s16x4 lo = lds_read_tr(p);
+      const s16x4 hi = lds_read_tr(p + 4 * T::VPITCH);
+      fr[r] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < (PF < N ? PF : N); ++r) read(r);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    hook(i);
+    if (i + PF < N) read(i + PF);
+    if (i < NS) {
+      s[i & 1] = mfma32<BF16>(fr[i], qreg[i >> 1], i < 2 ? f32x16{} : s[i & 1]);
+    } else {
+      const int x = i - NS;
+      oacc[x % T::DBLK] = mfma32<BF16>(fr[i], pb[x / T::DBLK], oacc[x % T::DBLK]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
+    const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE, int BH,
+    int Lq, int Lk, int nqt, float c, unsigned qsign) {
+  using T = Tile<D>;
+  using LY = Layout<D>;
+  using KP = DmaPlan<T::KINST, kRun, kDmaWaves>;
+  using VP = DmaPlan<T::VINST, kRun, kDmaWaves>;
+  __shared__ __attribute__((aligned(16))) char smem[LY::TOTAL];
+  auto kb = [&](int i) __attribute__((always_inline)) -> char* { return smem + ((i & 1) ? LY::K1 : LY::K0); };
+  auto vb = [&](int i) __attribute__((always_inline)) -> char* { return smem + ((i & 1) ? LY::V1 : LY::V0); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave 0..7, in an SGPR
+  const int grp = w >> 2;                                   // 0 leads, 1 lags and issues the DMA
+  const int wd = w & 3;                                     // DMA slot of a group-1 wave
+  const int n = lane & 31;  // query column of the S^T / O^T tiles owned by this lane
+  const int h = lane >> 5;  // which 8-wide k slice this lane feeds to the MFMA
+
+  // Workgroup -> (batch*head, query tile).  Workgroups are dealt to the 8
+  // XCDs round robin; remap so that consecutive logical tiles (the query
+  // tiles of one head, which stream the same K/V) share an XCD and its L2.
+  // Causal: heavier (later) query tiles of a head are dispatched first.
+  const int total = BH * nqt;
+  const int wg = blockIdx.x;
+  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+  const int bh = logical / nqt;
+  const int qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
+  const int q0 = qt * kRows;
+  const int off = Lk - Lq;  // bottom-right causal alignment
+
+  const unsigned short* Qh = Q + (size_t)bh * Lq * D;
+  const char* Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
+  const char* Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
+
+  const int q_last = min(q0 + kRows, Lq) - 1;
+  const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
+  const int nkv = (kv_end + BN - 1) / BN;  // tiles the workgroup streams
+  const int wq0 = q0 + 32 * w;             // first query of this wave
+  const int w_key_end = CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk;
+  // Tiles [0, w_nkv) are computed by this wave; tiles [0, j_mask) hold no
+  // masked key for it (the causal diagonal band and the Lk tail do).
+  const int w_nkv = __builtin_amdgcn_readfirstlane(wq0 < Lq ? (w_key_end + BN - 1) / BN : 0);
+  int j_mask = w_nkv;
+  if (CAUSAL) {
+    const int first_bad = wq0 + off - BN + 2;  // first kv0 whose last key passes the diagonal
+    j_mask = min(j_mask, first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN);
+  }
+  if (Lk % BN) j_mask = min(j_mask, Lk / BN);
+  j_mask = __builtin_amdgcn_readfirstlane(j_mask);
+
+  // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
+  const int qi = wq0 + n;
+  s16x8 qreg[T::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < T::KSTEPS; ++t) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 16 * t + 8 * h);
+    x ^= qsign;
+    qreg[t] = __builtin_bit_cast(s16x8, x);
+  }
+
+  // DMA of one K or V tile by group 1 (DmaPlan over its 4 waves); rows past
+  // Lk read row Lk-1 and the V slots of those rows are zeroed once landed.
+  unsigned k_src[KP::N];
+  unsigned v_src[VP::N];
+#pragma unroll
+  for (int i = 0; i < KP::N; ++i)
+    k_src[i] = dma_src_offset<D>(KP::inst(i, wd), lane, T::KSPR) + kDmaBias - KP::pos_in_run(i) * 1024u;
+#pragma unroll
+  for (int i = 0; i < VP::N; ++i)
+    v_src[i] = dma_src_offset<D>(VP::inst(i, wd), lane, T::VSPR) + kDmaBias - VP::pos_in_run(i) * 1024u;
+  auto biased = [](const char* p) __attribute__((always_inline)) {
+    return reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) - kDmaBias);
+  };
+  auto dma_k = [&](char* buf, int kv0) __attribute__((always_inline)) {
+    const char* g = biased(Kb + (size_t)kv0 * (D * 2));
+    if (kv0 + BN <= Lk)
+      dma_tile_whole<KP>(g, buf, k_src, wd);
+    else
+      dma_tile_ragged<D, KP>(g, buf, k_src, wd, Lk - kv0);
+  };
+  auto dma_v = [&](char* buf, int kv0) __attribute__((always_inline)) {
+    const char* g = biased(Vb + (size_t)kv0 * (D * 2));
+    if (kv0 + BN <= Lk)
+      dma_tile_whole<VP>(g, buf, v_src, wd);
+    else
+      dma_tile_ragged<D, VP>(g, buf, v_src, wd, Lk - kv0);
+  };
+  // Wait for this wave's DMA; zero the V slots of rows past Lk it filled.
+  auto land = [&](char* vbuf, int kv0) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (vbuf != nullptr && kv0 + BN > Lk) {
+#pragma unroll
+      for (int i = 0; i < VP::N; ++i) {
+        if (i < VP::U || wd < VP::X) {
+          const int slot = VP::inst(i, wd) * 64 + lane;
+          if (kv0 + slot / T::VSPR >= Lk) *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+
+  f32x16 oacc[T::DBLK];
+#pragma unroll
+  for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
+  // Reference maximum d of the row (base-2 scaled-score units) and this
+  // lane's part of the denominator s, both relative to that reference.
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  f32x16 sc[2];  // scores of the tile between the matrix and softmax phases
+  s16x8 pb[4];   // weights of the tile between the softmax and matrix phases
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sc[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = s16x8{};
+
+  // Tile row read by this lane for S^T: bits 2 and 3 of n swapped, so the
+  // accumulator register r of block blk holds key 32 blk + 16 (r/8) + 8 h + r%8.
+  const int prow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
+  const int g = lane >> 4, li = lane & 15;
+  const int k_lane = prow * T::KPITCH + 16 * h;
+  const int v_lane = (8 * h + (li >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (li & 3)) * 2;
+
+  // DMA of K_{j+2} and V_{j+1} by a group-0 wave, spread over the slots
+  // of its matrix phase (runs of kRun instructions; the extra instruction
+  // of an uneven split goes first).  Only for whole tiles; the other cases
+  // are issued in one go before the phase.
+  constexpr int NR = KP::RUNS + VP::RUNS;  // DMA runs per step (K first)
+  auto dma_hook = [&](const char* kg, char* kdst, const char* vg, char* vdst) __attribute__((always_inline)) {
+    return [=, &k_src, &v_src](int i) __attribute__((always_inline)) {
+      if (i == 0) {
+        if constexpr (KP::X != 0) {
+          if (wd < KP::X) dma_run<1>(kg, k_src + KP::U, lds_addr(kdst + KP::inst(KP::U, wd) * 1024));
+        }
+        if constexpr (VP::X != 0) {
+          if (wd < VP::X) dma_run<1>(vg, v_src + VP::U, lds_addr(vdst + VP::inst(VP::U, wd) * 1024));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        if (i == 2 + q * 28 / NR) {
+          if (q < KP::RUNS) {
+            const int i0 = KP::run_first(q);
+            dma_run_n(KP::run_len(q), kg, k_src + i0, lds_addr(kdst + KP::inst(i0, wd) * 1024));
+          } else {
+            const int i0 = VP::run_first(q - KP::RUNS);
+            dma_run_n(VP::run_len(q - KP::RUNS), vg, v_src + i0, lds_addr(vdst + VP::inst(i0, wd) * 1024));
+          }
+        }
+      }
+    };
+  };
+  auto no_hook = [](int) __attribute__((always_inline)) {};
+
+  // Matrix phase of step j: S_{j+1} and O~ += V_j P_j.  Every wave runs
+  // both products on every step so that the loop has one code path: a wave
+  // past its last tile computes scores it never uses (K buffers always hold
+  // finite key rows) and multiplies V_j (loaded, finite) by zero weights.
+  // Group 0 (issue = true) also issues the DMA of the tiles of step j+1.
+  // issue_tag: 0 none (group 1), 1 spread over the slots (K_{j+2} and
+  // V_{j+1} whole), 2 in one go before the phase (ragged or absent tiles).
+  auto matrix = [&](int j, auto issue_tag) __attribute__((always_inline)) {
+    constexpr int ISSUE = decltype(issue_tag)::value;
+    if constexpr (ISSUE == 1) {
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc,
+                                        dma_hook(biased(Kb + (size_t)(j + 2) * BN * (D * 2)), kb(j + 2),
+                                                 biased(Vb + (size_t)(j + 1) * BN * (D * 2)), vb(j + 1)));
+    } else {
+      if constexpr (ISSUE == 2) {
+        if (j + 2 < nkv) dma_k(kb(j + 2), (j + 2) * BN);
+        if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
+      }
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook);
+    }
+  };
+  auto matrix_first = [&]() __attribute__((always_inline)) {  // step -1: S_0 only
+    matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook);
+  };
+  using NoIssue = std::integral_constant<int, 0>;
+  using IssueSpread = std::integral_constant<int, 1>;
+  using IssueUpfront = std::integral_constant<int, 2>;
+
+  // The guide's running maximum d_k = max(d_{k-1}, max of chunk k), with a
+  // lag: the reference d moves to the new maximum only when a tile's
+  // maximum exceeds it by more than kTau (base 2); then O~ and s get the
+  // correction exp(d_old - d_new).  Otherwise d stays, the weights
+  // exp(a - d) are at most 2^kTau, and O~ / s is unchanged in real
+  // arithmetic (the correction holds for any reference).  The branch is
+  // taken by the whole wave if any of its rows needs it.
+  auto advance_max = [&](float m_tile) __attribute__((always_inline)) {
+    const bool grow = m_tile > m_ref + kTau;
+    if (__any(grow)) {
+      const float m_new = grow ? m_tile : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
+    }
+  };
+
+  // P = exp(a - d) for the 32 scores of this lane against the current
+  // reference, rounded to the MFMA type for the value product; returns the
+  // sum of the fp32 weights (the denominator sums those: exact LSE).
+  auto weights = [&]() __attribute__((always_inline)) -> float {
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int st = e >> 3, blk = st >> 1, r = 8 * (st & 1) + (e & 7);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
+      pb[st][e & 7] = (short)round16<BF16>(p);
+      psum += p;
+    }
+    return psum;
+  };
+
+  // Softmax phase of tile t (scores in sc).  Keys past Lk and (causal) past
+  // the diagonal get score -inf and so weight exp2(-inf) = 0 (the scale is
+  // positive here).  The weights are first taken against the current
+  // reference d; every weight of a lane is at most that lane's sum, so when
+  // no sum exceeds 2^kTau (and every row has a reference) the reference may
+  // stay, exactly as when the tile maximum is within kTau of it.  Otherwise
+  // (the maximum jumped, or an exponential overflowed to inf) the tile
+  // maximum is taken, the reference is advanced as above and the weights
+  // are recomputed; the scores are still in sc.  A tile this wave does not
+  // compute gets zero weights.
+  auto softmax_tile = [&](int t) __attribute__((always_inline)) {
+    if (t >= w_nkv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = s16x8{};
+      return;
+    }
+    if (t >= j_mask) {
+      // Per-lane key offset and query made opaque here, so the per-element
+      // bounds are not hoisted out of the tile loop (registers).
+      int hk = 8 * h, q = qi;
+      asm volatile("" : "+v"(hk), "+v"(q));
+      const int kv0 = t * BN;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * blk + 16 * (r >> 3) + hk + (r & 7);
+          const bool ok = key < Lk && (!CAUSAL || key <= q + off);
+          if (!ok) sc[blk][r] = -INFINITY;
+        }
+    }
+    float psum = weights();
+    if (__any(!(psum <= kTauWeight) || m_ref == -INFINITY)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          mx = fmaxf(mx, sc[blk][r]);
+          mx = fmaxf(mx, sc[blk][r + 1]);
+        }
+      mx = halves_max(mx);
+      advance_max((mx == -INFINITY) ? -INFINITY : mx * c);
+      psum = weights();
+    }
+    l_run += psum;
+  };
+
+  // ---- the two groups' schedules, as separate loops (each wave executes
+  //      the same sequence of barriers) ----
+  // Step j: group 0 runs matrix(j) then softmax(j+1); group 1 runs
+  // softmax(j) then matrix(j), half a step later.  Group 0 issues the DMA
+  // of K_{j+2} and V_{j+1} during its matrix phase and waits for it at the
+  // end of its softmax phase.  Step -1 computes S_0 only (and loads K_1,
+  // V_0); K_0 is loaded before it.
+  if (grp == 0) {
+    dma_k(kb(0), 0);
+    land(nullptr, 0);
+    barrier_lds();
+    if (1 < nkv) dma_k(kb(1), BN);
+    dma_v(vb(0), 0);
+    __builtin_amdgcn_s_setprio(1);
+    matrix_first();
+    barrier_lds();
+    __builtin_amdgcn_s_setprio(0);
+    softmax_tile(0);
+    land(vb(0), 0);
+    barrier_lds();
+    // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
+    const int j_spread = max(0, min(nkv - 2, Lk / BN - 2));
+    int j = 0;
+    for (; j < j_spread; ++j) {
+      __builtin_amdgcn_s_setprio(1);
+      matrix(j, IssueSpread{});
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(0);
+      softmax_tile(j + 1);
+      land(vb(j + 1), (j + 1) * BN);
+      barrier_lds();
+    }
+    for (; j < nkv; ++j) {
+      __builtin_amdgcn_s_setprio(1);
+      matrix(j, IssueUpfront{});
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(0);
+      softmax_tile(j + 1);
+      if (j + 1 < nkv) land(vb(j + 1), (j + 1) * BN);
+      barrier_lds();
+    }
+  } else {
+    barrier_lds();
+    barrier_lds();
+    __builtin_amdgcn_s_setprio(1);
+    matrix_first();
+    barrier_lds();
+    for (int j = 0; j < nkv; ++j) {
+      __builtin_amdgcn_s_setprio(0);
+      softmax_tile(j);
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(1);
+      matrix(j, NoIssue{});
+      barrier_lds();
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+
+  // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
+  // Each wave stages its 32 rows of O in LDS (the tile buffers are free after
+  // the last barrier) so that the global stores are whole 16-byte chunks of
+  // consecutive rows.
+  char* ob = smem + w * 32 * LY::OPITCH;
+  const float l_tot = halves_sum(l_run);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = 32 * db + 8 * jj + 4 * h;
+      const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
+                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
+      const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
+                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(ob + n * LY::OPITCH + d * 2) = make_uint2(lo, hi);
+    }
+  if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
+  barrier_lds();
+  constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+#pragma unroll
+  for (int i = 0; i < 32 / ROWS; ++i) {
+    const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
+    if (wq0 + row < Lq) *reinterpret_cast<u32x4*>(O + ((size_t)bh * Lq + wq0 + row) * D + chunk * 8) = v;
+  }
+}
+
+template <bool BF16, bool CAUSAL>
+hipError_t launch(const PrefillArgs& a, hipStream_t s) {
+  const int nqt = (a.Lq + kRows - 1) / kRows;
+  const unsigned qsign = a.neg ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL>), dim3(a.BH * nqt), dim3(kThreads), 0, s,
+                     static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
+                     static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse, a.BH, a.Lq,
+                     a.Lk, nqt, a.c, qsign);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s) {
+  if (dtype == 2) return causal ? launch<true, true>(a, s) : launch<true, false>(a, s);
+  return causal ? launch<false, true>(a, s) : launch<false, false>(a, s);
+}
+
+}  // namespace attn
