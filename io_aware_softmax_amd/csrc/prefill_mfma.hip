@@ -362,7 +362,7 @@ template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE,
-    int BH, int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd) {
+    int BH, int Lq, int Lk, int nqt, float c, unsigned qsign) {
   using T = Tile<D>;
   // K tiles and V tiles are double buffered in their own arrays, one tile out
   // of phase: step j reads K_{j+1} and V_j while K_{j+2} and V_{j+1} land.
@@ -371,42 +371,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) char vb0[T::VBYTES];
   __shared__ __attribute__((aligned(16))) char vb1[T::VBYTES];
 
-  // Workgroup -> work items (batch*head, query tile).  Workgroups are dealt
-  // to the 8 XCDs round robin.  The items are split into 8 contiguous ranges
-  // (the query tiles of a few heads, which stream the same K/V) and XCD x
-  // works on range x, so those tiles share its L2.  Within a range, item
-  // order is head-major; causal items of a head go heaviest first.
-  // slots_per_xcd == 0: one item per workgroup, item = workgroup index.
-  // Otherwise the S = slots_per_xcd workgroups of an XCD walk its range in
-  // rounds of S items, in snake order (slot s takes position s of even
-  // rounds and S-1-s of odd ones), which pairs heavy causal tiles with
-  // light ones.  A workgroup that owns several items runs them one after
-  // the other (persistent), so the grid is one resident wave of workgroups.
-  const int total = BH * nqt;
-  const int wg = blockIdx.x;
-  const int xcd = wg % 8, slot = wg / 8;
-  const int range_lo = xcd * items_per_xcd;
-  const int range_n = max(0, min(items_per_xcd, total - range_lo));
-  for (int round = 0;; ++round) {
-  int logical;
-  if (slots_per_xcd == 0) {
-    if (round > 0) break;
-    logical = wg;
-  } else {
-    const int pos = round * slots_per_xcd + ((round & 1) ? slots_per_xcd - 1 - slot : slot);
-    if (pos >= range_n) break;
-    logical = range_lo + pos;
-  }
-  // The previous item's epilogue staged O in the V buffers.
-  if (round > 0) __syncthreads();
-  // Lane-derived values are made opaque per item so that the compiler does
-  // not keep them (and all they feed) live across items (registers).
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in an SGPR
   const int n = lane & 31;  // query column of the S^T / O^T tiles owned by this lane
   const int h = lane >> 5;  // which 8-wide k slice this lane feeds to the MFMA
+
+  // Workgroup -> (batch*head, query tile).  Workgroups are dealt to the 8
+  // XCDs round robin; remap so that consecutive logical tiles (the query
+  // tiles of one head, which stream the same K/V) share an XCD and its L2.
+  // Causal: heavier (later) query tiles of a head are dispatched first.
+  const int total = BH * nqt;
+  const int wg = blockIdx.x;
+  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
   const int bh = logical / nqt;
   const int qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
   const int q0 = qt * BM;
@@ -718,41 +695,16 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     if (wq0 + row < Lq)
       *reinterpret_cast<u32x4*>(O + ((size_t)bh * Lq + wq0 + row) * D + chunk * 8) = v;
   }
-  }  // items
 }
 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   const int nqt = (a.Lq + BM - 1) / BM;
   const unsigned qsign = a.neg ? 0x80008000u : 0u;
-  const int total = a.BH * nqt;
-  // Resident workgroups of this kernel on the current device, per XCD.
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  int resident = 0;
-  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_mfma_kernel<BF16, D, CAUSAL>), NT,
-                          &resident);
-  if (e != hipSuccess) return e;
-  const int cap = resident / 8 * 8;
-  int grid, slots, per;
-  if (cap >= 8 && total > cap) {  // persistent: one resident wave of workgroups
-    grid = cap;
-    slots = cap / 8;
-    per = (total + 7) / 8;
-  } else if (total % 8 == 0) {  // one item each, contiguous ranges per XCD
-    grid = total;
-    slots = total / 8;
-    per = total / 8;
-  } else {
-    grid = total;
-    slots = 0;
-    per = 0;
-  }
-  hipLaunchKernelGGL((prefill_mfma_kernel<BF16, D, CAUSAL>), dim3(grid), dim3(NT), 0, s,
+  hipLaunchKernelGGL((prefill_mfma_kernel<BF16, D, CAUSAL>), dim3(a.BH * nqt), dim3(NT), 0, s,
                      static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
                      static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse,
-                     a.BH, a.Lq, a.Lk, nqt, a.c, qsign, slots, per);
+                     a.BH, a.Lq, a.Lk, nqt, a.c, qsign);
   return hipGetLastError();
 }
 

@@ -64,9 +64,12 @@ struct Layout {
   static constexpr int K1 = T::KBYTES;
   static constexpr int V0 = 2 * T::KBYTES;
   static constexpr int V1 = 2 * T::KBYTES + T::VBYTES;
-  static constexpr int TOTAL = 2 * (T::KBYTES + T::VBYTES);
+  static constexpr int KV = 2 * (T::KBYTES + T::VBYTES);
   static constexpr int OPITCH = D * 2 + 16;  // staging pitch of O rows
-  static_assert(kWaves * 32 * OPITCH <= TOTAL, "every wave's O rows fit in the tile buffers");
+  static constexpr int OST = KV;             // O staging, apart from the tiles so that the
+                                             // next item's tiles can land meanwhile
+  static constexpr int TOTAL = KV + kWaves * 32 * OPITCH;
+  static_assert(TOTAL <= 160 * 1024, "one workgroup per CU");
 };
 
 // Workgroup barrier that does not wait for outstanding vector-memory loads
@@ -124,7 +127,7 @@ template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE, int BH,
-    int Lq, int Lk, int nqt, float c, unsigned qsign) {
+    int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd) {
   using T = Tile<D>;
   using LY = Layout<D>;
   using KP = DmaPlan<T::KINST, kRun, kDmaWaves>;
@@ -141,50 +144,69 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   const int n = lane & 31;  // query column of the S^T / O^T tiles owned by this lane
   const int h = lane >> 5;  // which 8-wide k slice this lane feeds to the MFMA
 
-  // Workgroup -> (batch*head, query tile).  Workgroups are dealt to the 8
-  // XCDs round robin; remap so that consecutive logical tiles (the query
-  // tiles of one head, which stream the same K/V) share an XCD and its L2.
-  // Causal: heavier (later) query tiles of a head are dispatched first.
+  // Workgroup -> work items (batch*head, query tile of 256 rows).
+  // Workgroups are dealt to the 8 XCDs round robin.  The items are split
+  // into 8 contiguous ranges (the query tiles of a few heads, which stream
+  // the same K/V) and XCD x works on range x, so those tiles share its L2.
+  // Within a range the order is head-major, causal tiles of a head
+  // heaviest first.  slots_per_xcd == 0: one item per workgroup, item =
+  // workgroup index.  Otherwise the S = slots_per_xcd workgroups of an XCD
+  // walk its range in rounds of S items in snake order (slot s takes
+  // position s of even rounds and S-1-s of odd ones, pairing heavy causal
+  // tiles with light ones); a workgroup with several items runs them one
+  // after the other and loads the next item's first tiles and Q while it
+  // writes the current output.
   const int total = BH * nqt;
   const int wg = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
-  const int bh = logical / nqt;
-  const int qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
-  const int q0 = qt * kRows;
+  const int xcd = wg % 8, slot = wg / 8;
+  const int range_lo = xcd * items_per_xcd;
+  const int range_n = max(0, min(items_per_xcd, total - range_lo));
+  auto item_at = [&](int round) __attribute__((always_inline)) -> int {  // -1: none
+    if (slots_per_xcd == 0) return round == 0 ? wg : -1;
+    const int pos = round * slots_per_xcd + ((round & 1) ? slots_per_xcd - 1 - slot : slot);
+    return pos < range_n ? range_lo + pos : -1;
+  };
   const int off = Lk - Lq;  // bottom-right causal alignment
 
-  const unsigned short* Qh = Q + (size_t)bh * Lq * D;
-  const char* Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
-  const char* Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
-
-  const int q_last = min(q0 + kRows, Lq) - 1;
-  const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
-  const int nkv = (kv_end + BN - 1) / BN;  // tiles the workgroup streams
-  const int wq0 = q0 + 32 * w;             // first query of this wave
-  const int w_key_end = CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk;
-  // Tiles [0, w_nkv) are computed by this wave; tiles [0, j_mask) hold no
-  // masked key for it (the causal diagonal band and the Lk tail do).
-  const int w_nkv = __builtin_amdgcn_readfirstlane(wq0 < Lq ? (w_key_end + BN - 1) / BN : 0);
-  int j_mask = w_nkv;
-  if (CAUSAL) {
-    const int first_bad = wq0 + off - BN + 2;  // first kv0 whose last key passes the diagonal
-    j_mask = min(j_mask, first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN);
-  }
-  if (Lk % BN) j_mask = min(j_mask, Lk / BN);
-  j_mask = __builtin_amdgcn_readfirstlane(j_mask);
-
-  // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
-  const int qi = wq0 + n;
+  // Per-item values (wave-uniform ones in SGPRs).
+  int bh = 0, nkv = 0, wq0 = 0, w_nkv = 0, j_mask = 0, qi = 0;
+  const char* Kb = nullptr;
+  const char* Vb = nullptr;
   s16x8 qreg[T::KSTEPS];
+  auto setup = [&](int logical) __attribute__((always_inline)) {
+    bh = logical / nqt;
+    const int qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
+    const int q0 = qt * kRows;
+    Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
+    Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
+    const int q_last = min(q0 + kRows, Lq) - 1;
+    const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
+    nkv = __builtin_amdgcn_readfirstlane((kv_end + BN - 1) / BN);  // tiles the workgroup streams
+    wq0 = q0 + 32 * w;                                             // first query of this wave
+    const int w_key_end = CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk;
+    // Tiles [0, w_nkv) are computed by this wave; tiles [0, j_mask) hold no
+    // masked key for it (the causal diagonal band and the Lk tail do).
+    w_nkv = __builtin_amdgcn_readfirstlane(wq0 < Lq ? (w_key_end + BN - 1) / BN : 0);
+    int jm = w_nkv;
+    if (CAUSAL) {
+      const int first_bad = wq0 + off - BN + 2;  // first kv0 whose last key passes the diagonal
+      jm = min(jm, first_bad <= 0 ? 0 : (first_bad + BN - 1) / BN);
+    }
+    if (Lk % BN) jm = min(jm, Lk / BN);
+    j_mask = __builtin_amdgcn_readfirstlane(jm);
+    // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
+    qi = wq0 + n;
+    const unsigned short* Qh = Q + (size_t)bh * Lq * D;
 #pragma unroll
-  for (int t = 0; t < T::KSTEPS; ++t) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 16 * t + 8 * h);
-    x ^= qsign;
-    qreg[t] = __builtin_bit_cast(s16x8, x);
-  }
+    for (int t = 0; t < T::KSTEPS; ++t) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 16 * t + 8 * h);
+      x ^= qsign;
+      qreg[t] = __builtin_bit_cast(s16x8, x);
+    }
+  };
 
-  // DMA of one K or V tile by group 1 (DmaPlan over its 4 waves); rows past
+  // DMA of one K or V tile by group 0 (DmaPlan over its 4 waves); rows past
   // Lk read row Lk-1 and the V slots of those rows are zeroed once landed.
   unsigned k_src[KP::N];
   unsigned v_src[VP::N];
@@ -226,8 +248,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   };
 
   f32x16 oacc[T::DBLK];
-#pragma unroll
-  for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
   // Reference maximum d of the row (base-2 scaled-score units) and this
   // lane's part of the denominator s, both relative to that reference.
   float m_ref = -INFINITY;
@@ -388,90 +408,114 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     l_run += psum;
   };
 
-  // ---- the two groups' schedules, as separate loops (each wave executes
-  //      the same sequence of barriers) ----
-  // Step j: group 0 runs matrix(j) then softmax(j+1); group 1 runs
-  // softmax(j) then matrix(j), half a step later.  Group 0 issues the DMA
-  // of K_{j+2} and V_{j+1} during its matrix phase and waits for it at the
-  // end of its softmax phase.  Step -1 computes S_0 only (and loads K_1,
-  // V_0); K_0 is loaded before it.
-  if (grp == 0) {
+  // First tiles of an item (K_0, V_0, K_1), by group 0.
+  auto first_tiles = [&]() __attribute__((always_inline)) {
     dma_k(kb(0), 0);
-    land(nullptr, 0);
-    barrier_lds();
-    if (1 < nkv) dma_k(kb(1), BN);
     dma_v(vb(0), 0);
-    __builtin_amdgcn_s_setprio(1);
-    matrix_first();
-    barrier_lds();
-    __builtin_amdgcn_s_setprio(0);
-    softmax_tile(0);
-    land(vb(0), 0);
-    barrier_lds();
-    // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
-    const int j_spread = max(0, min(nkv - 2, Lk / BN - 2));
-    int j = 0;
-    for (; j < j_spread; ++j) {
-      __builtin_amdgcn_s_setprio(1);
-      matrix(j, IssueSpread{});
-      barrier_lds();
-      __builtin_amdgcn_s_setprio(0);
-      softmax_tile(j + 1);
-      land(vb(j + 1), (j + 1) * BN);
-      barrier_lds();
-    }
-    for (; j < nkv; ++j) {
-      __builtin_amdgcn_s_setprio(1);
-      matrix(j, IssueUpfront{});
-      barrier_lds();
-      __builtin_amdgcn_s_setprio(0);
-      softmax_tile(j + 1);
-      if (j + 1 < nkv) land(vb(j + 1), (j + 1) * BN);
-      barrier_lds();
-    }
-  } else {
-    barrier_lds();
-    barrier_lds();
-    __builtin_amdgcn_s_setprio(1);
-    matrix_first();
-    barrier_lds();
-    for (int j = 0; j < nkv; ++j) {
-      __builtin_amdgcn_s_setprio(0);
-      softmax_tile(j);
-      barrier_lds();
-      __builtin_amdgcn_s_setprio(1);
-      matrix(j, NoIssue{});
-      barrier_lds();
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
+    if (1 < nkv) dma_k(kb(1), BN);
+  };
 
-  // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
-  // Each wave stages its 32 rows of O in LDS (the tile buffers are free after
-  // the last barrier) so that the global stores are whole 16-byte chunks of
-  // consecutive rows.
-  char* ob = smem + w * 32 * LY::OPITCH;
-  const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
+  int round = 0;
+  int logical = item_at(0);
+  if (logical < 0) return;  // the whole workgroup: no barrier pending
+  setup(logical);
+  if (grp == 0) {
+    first_tiles();
+    land(vb(0), 0);
+  }
+  for (;;) {
 #pragma unroll
-  for (int db = 0; db < T::DBLK; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d = 32 * db + 8 * jj + 4 * h;
-      const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
-                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
-      const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
-                          ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(ob + n * LY::OPITCH + d * 2) = make_uint2(lo, hi);
+    for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
+    m_ref = -INFINITY;
+    l_run = 0.f;
+    barrier_lds();  // the item's first tiles have landed
+
+    // ---- the two groups' schedules, as separate loops (each wave executes
+    //      the same sequence of barriers) ----
+    // Step j: group 0 runs matrix(j) then softmax(j+1); group 1 runs
+    // softmax(j) then matrix(j), half a step later.  Group 0 issues the DMA
+    // of K_{j+2} and V_{j+1} during its matrix phase and waits for it at
+    // the end of its softmax phase.  Step -1 computes S_0 only.
+    if (grp == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      matrix_first();
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(0);
+      softmax_tile(0);
+      barrier_lds();
+      // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
+      const int j_spread = max(0, min(nkv - 2, Lk / BN - 2));
+      int j = 0;
+      for (; j < j_spread; ++j) {
+        __builtin_amdgcn_s_setprio(1);
+        matrix(j, IssueSpread{});
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile(j + 1);
+        land(vb(j + 1), (j + 1) * BN);
+        barrier_lds();
+      }
+      for (; j < nkv; ++j) {
+        __builtin_amdgcn_s_setprio(1);
+        matrix(j, IssueUpfront{});
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile(j + 1);
+        if (j + 1 < nkv) land(vb(j + 1), (j + 1) * BN);
+        barrier_lds();
+      }
+    } else {
+      barrier_lds();
+      __builtin_amdgcn_s_setprio(1);
+      matrix_first();
+      barrier_lds();
+      for (int j = 0; j < nkv; ++j) {
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile(j);
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(1);
+        matrix(j, NoIssue{});
+        barrier_lds();
+      }
     }
-  if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
-  barrier_lds();
-  constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+    __builtin_amdgcn_s_setprio(0);
+
+    // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
+    // Each wave stages its 32 rows of O in LDS so that the global stores are
+    // whole 16-byte chunks of consecutive rows; the next item's first tiles
+    // and Q are loaded meanwhile (all tile reads of this item are done).
+    char* ob = smem + LY::OST + w * 32 * LY::OPITCH;
+    const float l_tot = halves_sum(l_run);
+    const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int i = 0; i < 32 / ROWS; ++i) {
-    const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
-    if (wq0 + row < Lq) *reinterpret_cast<u32x4*>(O + ((size_t)bh * Lq + wq0 + row) * D + chunk * 8) = v;
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = 32 * db + 8 * jj + 4 * h;
+        const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
+        const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(ob + n * LY::OPITCH + d * 2) = make_uint2(lo, hi);
+      }
+    if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
+    unsigned short* Ow = O + ((size_t)bh * Lq + wq0) * D;  // this wave's rows
+    const int rows_left = Lq - wq0;
+    logical = item_at(++round);
+    if (logical >= 0) {
+      setup(logical);
+      if (grp == 0) first_tiles();
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staged rows
+    constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
+      if (row < rows_left) *reinterpret_cast<u32x4*>(Ow + (size_t)row * D + chunk * 8) = v;
+    }
+    if (logical < 0) break;
+    if (grp == 0) land(vb(0), 0);
   }
 }
 
@@ -479,10 +523,33 @@ template <bool BF16, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a, hipStream_t s) {
   const int nqt = (a.Lq + kRows - 1) / kRows;
   const unsigned qsign = a.neg ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL>), dim3(a.BH * nqt), dim3(kThreads), 0, s,
+  const int total = a.BH * nqt;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int resident = 0;
+  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_pp_kernel<BF16, 128, CAUSAL>), kThreads,
+                          &resident);
+  if (e != hipSuccess) return e;
+  const int cap = resident / 8 * 8;
+  int grid, slots, per;
+  if (cap >= 8 && total > cap) {  // persistent: one resident wave of workgroups
+    grid = cap;
+    slots = cap / 8;
+    per = (total + 7) / 8;
+  } else if (total % 8 == 0) {  // one item each, contiguous ranges per XCD
+    grid = total;
+    slots = total / 8;
+    per = total / 8;
+  } else {
+    grid = total;
+    slots = 0;
+    per = 0;
+  }
+  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
                      static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse, a.BH, a.Lq,
-                     a.Lk, nqt, a.c, qsign);
+                     a.Lk, nqt, a.c, qsign, slots, per);
   return hipGetLastError();
 }
 
