@@ -210,8 +210,8 @@ def main():
         rec["ms_prefill_min"] = float(np.min(p_ms))
         rec["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                           "traffic": _traffic("prefill_mfma.hip", "prefill_causal_bf16_8k_traffic.txt"),
-                           "kernel": "prefill_mfma_kernel<bf16, D=128, causal>"}
+                           "traffic": _traffic("prefill_pp.hip", "prefill_causal_bf16_8k_traffic.txt"),
+                           "kernel": "prefill_pp_kernel<bf16, D=128, causal>"}
     if run_d:
         gbs = wd.kv_bytes() / (d_avg * 1e-3) / 1e9
         rec["decode"] = {"metric": "decode HBM GB/s (K+V bytes / decode call time)", "value": gbs,

@@ -56,6 +56,13 @@ constexpr int kDmaWaves = 4;        // group 1 issues the DMA
 // maximum: weights exp(a - d) stay below 2^8.
 constexpr float kTau = 8.f;
 constexpr float kTauWeight = 256.f;  // 2^kTau
+// Headroom (base 2) of a new reference above the tile maximum that set it.
+// bf16 weights keep the fp32 exponent range, so a reference 24 above the
+// maximum (weights down to 2^-24 at first) costs no precision and makes
+// later maxima rarely pass it; fp16 weights would leave the fp16 range, so
+// there the reference is the maximum itself.
+template <bool BF16>
+constexpr float kHeadroom = BF16 ? 24.f : 0.f;
 
 template <int D>
 struct Layout {
@@ -325,25 +332,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   using IssueSpread = std::integral_constant<int, 1>;
   using IssueUpfront = std::integral_constant<int, 2>;
 
-  // The guide's running maximum d_k = max(d_{k-1}, max of chunk k), with a
-  // lag: the reference d moves to the new maximum only when a tile's
-  // maximum exceeds it by more than kTau (base 2); then O~ and s get the
-  // correction exp(d_old - d_new).  Otherwise d stays, the weights
-  // exp(a - d) are at most 2^kTau, and O~ / s is unchanged in real
-  // arithmetic (the correction holds for any reference).  The branch is
-  // taken by the whole wave if any of its rows needs it.
-  auto advance_max = [&](float m_tile) __attribute__((always_inline)) {
-    const bool grow = m_tile > m_ref + kTau;
-    if (__any(grow)) {
-      const float m_new = grow ? m_tile : m_ref;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
-    }
-  };
-
   // P = exp(a - d) for the 32 scores of this lane against the current
   // reference, rounded to the MFMA type for the value product; returns the
   // sum of the fp32 weights (the denominator sums those: exact LSE).
@@ -363,13 +351,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // Softmax phase of tile t (scores in sc).  Keys past Lk and (causal) past
   // the diagonal get score -inf and so weight exp2(-inf) = 0 (the scale is
   // positive here).  The weights are first taken against the current
-  // reference d; every weight of a lane is at most that lane's sum, so when
-  // no sum exceeds 2^kTau (and every row has a reference) the reference may
-  // stay, exactly as when the tile maximum is within kTau of it.  Otherwise
-  // (the maximum jumped, or an exponential overflowed to inf) the tile
-  // maximum is taken, the reference is advanced as above and the weights
-  // are recomputed; the scores are still in sc.  A tile this wave does not
-  // compute gets zero weights.
+  // reference d.  Every weight of a lane is at most that lane's sum, so when
+  // no sum exceeds 2^kTau (and every row has a reference) the weights stay
+  // within 2^kTau and the reference may stay.  Otherwise (a maximum jumped,
+  // or an exponential overflowed to inf) the tile maximum is taken, the
+  // reference advanced and the weights recomputed; the scores are still in
+  // sc.  A tile this wave does not compute gets zero weights.
   auto softmax_tile = [&](int t) __attribute__((always_inline)) {
     if (t >= w_nkv) {
 #pragma unroll
@@ -402,7 +389,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
           mx = fmaxf(mx, sc[blk][r + 1]);
         }
       mx = halves_max(mx);
-      advance_max((mx == -INFINITY) ? -INFINITY : mx * c);
+      // The guide's running maximum d_k = max(d_{k-1}, max of chunk k)
+      // with headroom: a row whose tile maximum passed its reference moves
+      // the reference kHeadroom above that maximum and corrects O~ and s by
+      // exp(d_old - d_new); exact for any reference, and later tiles may
+      // rise kHeadroom + kTau before they come back here.
+      const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+      const bool grow = m_tile > m_ref;
+      const float m_new = grow ? m_tile + kHeadroom<BF16> : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
       psum = weights();
     }
     l_run += psum;
