@@ -59,13 +59,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 }
 
 // ATTN_PREFILL_KERNEL=single forces the single-group 16-bit prefill kernel
-// everywhere (tests compare the two kernels); read once.
+// everywhere (tests compare the two kernels); read on every call.
 int prefill_variant() {
-  static const int v = [] {
-    const char* e = std::getenv("ATTN_PREFILL_KERNEL");
-    return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
-  }();
-  return v;
+  const char* e = std::getenv("ATTN_PREFILL_KERNEL");
+  return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
 }
 
 int auto_splits(int64_t BH, int Lk) {

@@ -1,0 +1,114 @@
+"""GPU parity of the prefill kernels' own paths, against the float64 oracle.
+
+16-bit inputs at D = 128 run the two-group kernel; ATTN_PREFILL_KERNEL=single
+sends them to the single-group kernel instead, so both are checked on the
+same inputs.  The two-group kernel moves a row's reference maximum only when
+a lane's weight sum passes 2^8 (for bf16 then 24 above the tile maximum);
+the cases below force that path on every few tiles (scores rising along the
+keys), never after the first tile (falling scores), and through an
+exponential that overflows to inf (scores of thousands).  The item schedule
+has three branches (one item per workgroup with and without per-XCD ranges,
+persistent workgroups over uneven ranges); each gets a case.  Bounds are the
+documented ones: max |dO| 1e-2 (fp16), 2e-2 (bf16); LSE within
+1e-4 * max(1, |LSE_ref|).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_softmax_amd import inputs
+from tests.gpu_common import O_TOL, compare, require_gpu, say, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import io_aware_softmax_amd as m
+    m.load()
+    yield
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _fwd(vals, dtype, causal, scale):
+    import torch
+    from io_aware_softmax_amd import binding
+    q, k, v = (to_device(inputs.round_to(vals[t], dtype), dtype) for t in "qkv")
+    O, L = binding.attn_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_host_f64(O), to_host_f64(L)
+
+
+def _exact(vals, dtype):
+    """float32 values of the rounded inputs (what both sides compute on)."""
+    return {t: inputs.to_float32(inputs.round_to(vals[t], dtype), dtype) for t in "qkv"}
+
+
+def _check(name, vals, dtype, causal, scale):
+    ex = _exact(vals, dtype)
+    Or, Lr = oracle.attention(ex["q"], ex["k"], ex["v"], scale, causal)
+    O, L = _fwd(vals, dtype, causal, scale)
+    return compare(name, dtype, O, L, Or, Lr), O
+
+
+def _normal(shape, seed):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape, dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_kernels_agree(dtype, causal, monkeypatch):
+    """Both 16-bit prefill kernels at D = 128 on several tiles and a ragged tail."""
+    B, H, L, D = 1, 4, 700, 128
+    vals = {t: _normal((B, H, L, D), 500 + i + 10 * causal) for i, t in enumerate("qkv")}
+    scale = 1.0 / np.sqrt(D)
+    say(f"case kernels agree {dtype} causal={causal}")
+    _, O_two = _check(f"two-group {dtype} c{int(causal)}", vals, dtype, causal, scale)
+    monkeypatch.setenv("ATTN_PREFILL_KERNEL", "single")
+    _, O_one = _check(f"single-group {dtype} c{int(causal)}", vals, dtype, causal, scale)
+    assert np.max(np.abs(O_two - O_one)) <= 2 * O_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("pattern", ["rising", "falling"])
+def test_reference_moves(dtype, pattern):
+    """Row maxima that rise tile after tile (the reference moves every few
+    tiles) or fall (only the first tile sets it)."""
+    B, H, L, D = 1, 2, 1500, 128
+    q = 0.1 * _normal((B, H, L, D), 601)
+    k = 0.1 * _normal((B, H, L, D), 602)
+    v = _normal((B, H, L, D), 603)
+    q[..., 0] = 1.0
+    ramp = np.arange(L, dtype=np.float32) * 0.4  # scores up to ~ 600 / sqrt(128) along the keys
+    k[..., 0] = ramp if pattern == "rising" else ramp[::-1]
+    vals = {"q": q, "k": k, "v": v}
+    say(f"case reference moves {dtype} {pattern}")
+    for causal in (False, True):
+        _check(f"{pattern} {dtype} c{int(causal)}", vals, dtype, causal, 1.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_huge_scores_overflow_path(dtype):
+    """Scale 40: scaled scores of thousands, so the first weights of a tile
+    overflow to inf and the tile is redone from its maximum."""
+    B, H, L, D = 1, 2, 400, 128
+    vals = {t: _normal((B, H, L, D), 700 + i) for i, t in enumerate("qkv")}
+    say(f"case huge scores {dtype}")
+    for causal in (False, True):
+        _check(f"huge {dtype} c{int(causal)}", vals, dtype, causal, 40.0)
+
+
+@pytest.mark.parametrize("H,L,causal", [(257, 256, False), (37, 1024, True), (8, 512, True)])
+def test_item_schedules(H, L, causal):
+    """257 query tiles: more than one resident wave of workgroups, ranges of
+    33 items with a short last one.  37 heads x 4 tiles: one item per
+    workgroup, count not a multiple of 8.  8 x 2: one item per workgroup in
+    per-XCD ranges."""
+    B, D = 1, 128
+    vals = {t: _normal((B, H, L, D), 800 + i + H) for i, t in enumerate("qkv")}
+    say(f"case item schedule H{H} L{L} causal={causal}")
+    _check(f"schedule H{H} L{L}", vals, "bf16", causal, 1.0 / np.sqrt(D))
