@@ -98,20 +98,10 @@ __device__ __forceinline__ unsigned lds_addr(const char* p) {
 // Completion is awaited explicitly with s_waitcnt vmcnt(0).
 constexpr unsigned kDmaBias = 4096u;
 
-// Wave-uniform copy of a pointer (the operands below are SGPRs).
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uintptr_t u = reinterpret_cast<uintptr_t>(p);
-  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
-  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
-  return reinterpret_cast<const char*>(((uintptr_t)hi << 32) | lo);
-}
-
+// gbase and m0 must be wave-uniform (SGPR operands).
 template <int G>
-__device__ __forceinline__ void dma_run(const char* gbase_in, const unsigned* voff, unsigned m0_in) {
+__device__ __forceinline__ void dma_run(const char* gbase, const unsigned* voff, unsigned m0) {
   static_assert(G >= 1 && G <= 4, "one M0 run holds 1 to 4 instructions");
-  // Both are wave-uniform by construction; the copies keep them in SGPRs.
-  const char* gbase = uniform_ptr(gbase_in);
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(m0_in);
   if constexpr (G == 1)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n"
                  :
