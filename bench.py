@@ -220,6 +220,27 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS,
                                       "traffic": _traffic("decode.hip", "decode_bf16_32k_traffic.txt"),
                                       "kernel": "decode_split_kernel<bf16, D=128> + decode_combine_kernel"}}
+    if run_d:
+        # Not part of the step: the ragged-length KV-cache decode on the same
+        # cache, with seeded per-sequence lengths in [1, Lk]; bytes are the
+        # K+V rows actually attended.
+        lens = inputs.ragged_lengths(4, wd.B, wd.Lk)
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        for _ in range(10):
+            binding.attn_decode_varlen_fwd(qd, kd, vd, sl, scale=wd.scale, out=od, lse=ld)
+        torch.cuda.synchronize()
+        vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in vev:
+            a.record(stream)
+            binding.attn_decode_varlen_fwd(qd, kd, vd, sl, scale=wd.scale, out=od, lse=ld)
+            b.record(stream)
+        torch.cuda.synchronize()
+        v_ms = float(np.mean([a.elapsed_time(b) for a, b in vev]))
+        v_bytes = int(lens.astype(np.int64).sum()) * wd.H * 2 * wd.D * 2
+        rec["decode_varlen"] = {"metric": "ragged KV-cache decode HBM GB/s (attended K+V bytes / call time)",
+                                "value": v_bytes / (v_ms * 1e-3) / 1e9, "unit": "GB/s", "ms": v_ms,
+                                "bytes": v_bytes, "lengths": "seeded uniform in [1, 32768] per sequence",
+                                "frac_of_hbm_peak": v_bytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
                      "arch": getattr(props, "gcnArchName", "")}
     rec["input_gen_s"] = gen_s

@@ -66,7 +66,7 @@ typedef enum {
   ATTN_ERR_HIP = -10            /* a HIP launch or allocation failed */
 } attn_status_t;
 
-/* Largest split count accepted by attn_decode_fwd. */
+/* Largest split count accepted by attn_decode_fwd and attn_decode_varlen_fwd. */
 #define ATTN_MAX_SPLITS 256
 
 /*
@@ -104,6 +104,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Lk, int D, float scale, int num_splits,
                     void* stream, int dtype);
+
+/*
+ * attn_decode_varlen_fwd - single-query attention over a KV cache whose
+ * sequences have different lengths (the decode step of generation, which
+ * the quidproquo.cc guide, slide 5, separates from the prefill).
+ *
+ * q and o are [B,H,1,D]; k and v are [B,H,Lk_max,D] caches; lse is
+ * [B,H,1].  seqlens is a DEVICE pointer to B int32 lengths (4-byte
+ * aligned, read when the stream reaches the call): (b, h) attends to its
+ * first seqlens[b] keys only, and rows past that length are never read
+ * (they may hold anything).  A length is clamped to [0, Lk_max]; a length of
+ * 0 gives o = 0 and lse = -inf.  The keys of each (b, h) are cut into
+ * num_splits ranges of ceil(len / num_splits) keys and merged as in
+ * attn_decode_fwd; num_splits == 0 lets the library choose from Lk_max.
+ * Workspace as for attn_fwd.  seqlens must not overlap o or lse.
+ */
+int attn_decode_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const int* seqlens, int B, int H, int Lk_max, int D, float scale,
+                           int num_splits, void* stream, int dtype);
 
 /*
  * attn_decode_auto_splits - the split count attn_fwd and attn_decode_fwd

@@ -22,7 +22,7 @@ LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
-EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_auto_splits", "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_decode_auto_splits", "attn_strerror")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
         lib.attn_decode_fwd.restype = i
+        lib.attn_decode_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
+        lib.attn_decode_varlen_fwd.restype = i
         lib.attn_decode_auto_splits.argtypes = [i, i, i, i]
         lib.attn_decode_auto_splits.restype = i
         lib.attn_strerror.argtypes = [i]
@@ -136,6 +138,32 @@ def attn_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Op
     _check(lib.attn_decode_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), B, H, Lk, D, scale, int(num_splits),
                                _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return out, lse
+
+
+def attn_decode_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor,
+                           scale: Optional[float] = None, num_splits: int = 0,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Single-query attention over a KV cache with per-sequence lengths,
+    through ``attn_decode_varlen_fwd``.
+
+    q [B,H,1,D]; k and v [B,H,Lk_max,D]; seqlens an int32 GPU tensor [B]
+    (each clamped to [0, Lk_max] by the library).
+    """
+    lib = load()
+    B, H, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("attn_decode_varlen_fwd takes one query per (batch, head)")
+    if (not isinstance(seqlens, torch.Tensor) or not seqlens.is_cuda or seqlens.dtype != torch.int32
+            or seqlens.shape != (B,) or not seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    Lk = k.shape[2]
+    out, lse = _prep(q, k, v, out, lse, 1)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_decode_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), seqlens.data_ptr(), B, H, Lk, D, scale,
+                                      int(num_splits), _stream_handle(stream), _DTYPE_CODES[q.dtype]))
     return out, lse
 
 

@@ -78,7 +78,8 @@ int auto_splits(int64_t BH, int Lk) {
 }
 
 int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int Lk, int D, float scale, int splits, hipStream_t stream, int dtype) {
+               int Lk, int D, float scale, int splits, hipStream_t stream, int dtype,
+               const int* seqlens = nullptr) {
   const int64_t BH = int64_t(B) * H;
   if (splits == 0) splits = auto_splits(BH, Lk);
   if (BH * splits > kMaxWorkgroups) return ATTN_ERR_DIM;
@@ -97,7 +98,9 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   a.part_m = a.part_o + nparts * D;
   a.part_l = a.part_m + nparts;
   a.BH = int(BH);
+  a.H = H;
   a.Lk = Lk;
+  a.seqlens = seqlens;
   a.splits = splits;
   a.keys_per_split = int((int64_t(Lk) + splits - 1) / splits);
   a.c = std::fabs(scale) * attn::kLog2e;
@@ -152,6 +155,22 @@ ATTN_EXPORT int attn_decode_fwd(const void* q, const void* k, const void* v, voi
   if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
   return run_decode(q, k, v, o, lse, B, H, Lk, D, scale, num_splits, static_cast<hipStream_t>(stream),
                     dtype);
+}
+
+ATTN_EXPORT int attn_decode_varlen_fwd(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const int* seqlens, int B, int H, int Lk_max,
+                                       int D, float scale, int num_splits, void* stream,
+                                       int dtype) {
+  if (seqlens == nullptr) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(seqlens) & 3u) return ATTN_ERR_ALIGN;
+  const int st = validate(q, k, v, o, lse, B, H, 1, Lk_max, D, 0, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  const size_t no = size_t(B) * H * D * elem_bytes(dtype), nl = size_t(B) * H * sizeof(float);
+  if (overlaps(o, no, seqlens, size_t(B) * sizeof(int)) || overlaps(lse, nl, seqlens, size_t(B) * sizeof(int)))
+    return ATTN_ERR_ALIAS;
+  return run_decode(q, k, v, o, lse, B, H, Lk_max, D, scale, num_splits,
+                    static_cast<hipStream_t>(stream), dtype, seqlens);
 }
 
 ATTN_EXPORT int attn_decode_auto_splits(int B, int H, int Lk, int D) {

@@ -33,9 +33,11 @@ struct DecodeArgs {
   float* part_m;  // [BH, splits] partial maxima, base-2 scaled-score units
   float* part_l;  // [BH, splits] partial denominators
   int BH;
-  int Lk;
+  int H;
+  int Lk;              // keys per (b, h) in memory (the row stride of k and v)
+  const int* seqlens;  // device [B] lengths (clamped to [0, Lk]) or nullptr: all Lk
   int splits;
-  int keys_per_split;
+  int keys_per_split;  // used when seqlens == nullptr
   float c;
   bool neg;
 };

@@ -20,7 +20,12 @@
 // chunks of the guide's output correction:
 //   d = max_p d_p,  s = sum_p s_p exp(d_p - d),
 //   O = sum_p O_p (s_p / s) exp(d_p - d),  lse = d + ln s.
-// Empty ranges (s_p = 0) are skipped.
+// Empty ranges (s_p = 0) are skipped; a (b, h) with no key at all gets
+// O = 0 and lse = -inf (the empty sum).
+//
+// With per-sequence lengths (a KV cache whose rows past a sequence's length
+// are unused), the same kernels run over the first seqlens[b] keys of each
+// (b, h), cut into `splits` ranges of that length.
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -113,7 +118,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(NT) void decode_split_kernel(
     const u32x4* __restrict__ Q, const u32x4* __restrict__ K, const u32x4* __restrict__ V,
     float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l, int Lk,
-    int keys_per_split, int splits, float c, float qsign) {
+    int keys_per_split, int splits, float c, float qsign, const int* __restrict__ seqlens, int H) {
   using E = Elem<DT>;
   constexpr int EPL = E::PER16;       // elements per lane per key
   constexpr int LPK = D / EPL;        // lanes per key row
@@ -130,8 +135,15 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kq = lane / LPK, dl = lane % LPK;
 
-  const int kb = min(Lk, split * keys_per_split);
-  const int ke = min(Lk, kb + keys_per_split);
+  // Keys of this (b, h): all Lk, or the first seqlens[b] of them (a KV
+  // cache with ragged lengths), cut into `splits` equal ranges.
+  int len = Lk, kps = keys_per_split;
+  if (seqlens != nullptr) {
+    len = min(max(seqlens[bh / H], 0), Lk);
+    kps = (len + splits - 1) / splits;
+  }
+  const int kb = min(len, split * kps);
+  const int ke = min(len, kb + kps);
 
   // Query slice, pre-multiplied by |scale| log2(e) (and the sign of scale).
   float qf[EPL];
@@ -256,7 +268,7 @@ hipError_t launch_dt(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_split_kernel<DT, D>), dim3(a.splits * a.BH), dim3(NT), 0, s,
                      static_cast<const u32x4*>(a.q), static_cast<const u32x4*>(a.k),
                      static_cast<const u32x4*>(a.v), a.part_o, a.part_m, a.part_l, a.Lk,
-                     a.keys_per_split, a.splits, a.c, a.neg ? -1.f : 1.f);
+                     a.keys_per_split, a.splits, a.c, a.neg ? -1.f : 1.f, a.seqlens, a.H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<DT, D>), dim3(a.BH), dim3(D), 0, s, a.part_o, a.part_m,

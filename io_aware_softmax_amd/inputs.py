@@ -176,3 +176,10 @@ def sample_rows(wl: Workload, h: int, n: int = 256) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed_words[0], 1, h])))
     mid = g.choice(np.arange(1, L - 1), size=n - 2, replace=False)
     return np.sort(np.concatenate([[0, L - 1], mid])).astype(np.int64)
+
+
+def ragged_lengths(seed: int, B: int, Lk_max: int, lo: int = 1) -> np.ndarray:
+    """Per-sequence KV-cache lengths for ragged decode: B int32 values drawn
+    uniformly from [lo, Lk_max] by ``SeedSequence([seed, 3])``."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    return rng.integers(lo, Lk_max + 1, size=B, dtype=np.int64).astype(np.int32)

@@ -25,6 +25,7 @@ partition for L <= 8 across the independent recurrences below.
 
 from .attention import (  # noqa: F401
     attention,
+    decode_varlen,
     one_pass_chunked,
     tiled_outer_kv,
     two_pass_chunked,

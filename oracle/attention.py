@@ -38,6 +38,7 @@ import numpy as np
 
 __all__ = [
     "attention",
+    "decode_varlen",
     "two_pass_chunked",
     "one_pass_chunked",
     "decoupled_softmax",
@@ -121,6 +122,39 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
                 LSE[b, h, r0:r0 + len(rr)] = m + np.log(s)
                 if check:
                     _check_block(p, o, m, m + np.log(s), allowed, vv)
+    return O, LSE
+
+
+def decode_varlen(q, k, v, seqlens, scale: float):
+    """Single-query attention over caches with per-sequence lengths, float64.
+
+    The decode step of the guide's prefill/decode split (slide 5) over a key
+    cache: query ``q[b, h, 0]`` attends to the first ``seqlens[b]`` keys of
+    ``k[b, h]`` and nothing else.  Each sequence is the plain definition
+    (``attention`` on the sliced keys).  Readings of the interface: a length
+    is clamped to ``[0, Lk]``; a sequence with no key gets O = 0 and
+    LSE = -inf (the empty sum).
+
+    Args:
+      q: [B, H, 1, D]; k, v: [B, H, Lk, D]; seqlens: B integers.
+    Returns:
+      (O [B, H, 1, D], LSE [B, H, 1]) in float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, Lq, D = q.shape
+    if Lq != 1:
+        raise ValueError("decode_varlen takes one query per (batch, head)")
+    Lk = k.shape[2]
+    lens = np.clip(np.asarray(seqlens, dtype=np.int64).reshape(B), 0, Lk)
+    O = np.zeros((B, H, 1, D), dtype=np.float64)
+    LSE = np.full((B, H, 1), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        O[b:b + 1], LSE[b:b + 1] = attention(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], scale)
     return O, LSE
 
 

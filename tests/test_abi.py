@@ -96,6 +96,14 @@ def test_validation_errors(lib):
     assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 48, 0.1, 4, None, 2) == e["ATTN_ERR_UNSUPPORTED_D"]
     assert d(G, 0, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, 4, None, 2) == e["ATTN_ERR_NULL"]
     assert d(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 0, 64, 0.1, 4, None, 2) == e["ATTN_ERR_DIM"]
+    # ragged-length decode entry point (seqlens at 6 G)
+    r = lib.attn_decode_varlen_fwd
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 0, 2, 3, 100, 64, 0.1, 0, None, 2) == e["ATTN_ERR_NULL"]
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 6 * G + 2, 2, 3, 100, 64, 0.1, 0, None, 2) == e["ATTN_ERR_ALIGN"]
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 6 * G, 2, 3, 100, 64, 0.1, 300, None, 2) == e["ATTN_ERR_SPLITS"]
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 6 * G, 2, 3, 0, 64, 0.1, 0, None, 2) == e["ATTN_ERR_DIM"]
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 4 * G + 8, 2, 3, 100, 64, 0.1, 0, None, 2) == e["ATTN_ERR_ALIAS"]
+    assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 5 * G, 2, 3, 100, 64, 0.1, 0, None, 2) == e["ATTN_ERR_ALIAS"]
 
 
 def test_strerror_and_auto_splits(lib):

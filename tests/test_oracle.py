@@ -335,3 +335,55 @@ def test_planted_transpose_is_caught():
     O, _ = oracle.attention(q, k, v, 0.5)
     Ot, _ = oracle.attention(k, q, v, 0.5)
     assert np.max(np.abs(O - Ot)) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Decode over caches with per-sequence lengths
+# --------------------------------------------------------------------------
+
+def test_decode_varlen_full_lengths_equal_attention():
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((3, 2, 1, 16))
+    k = rng.standard_normal((3, 2, 40, 16))
+    v = rng.standard_normal((3, 2, 40, 16))
+    O, L = oracle.decode_varlen(q, k, v, [40, 40, 40], 0.3)
+    Or, Lr = oracle.attention(q, k, v, 0.3)
+    np.testing.assert_array_equal(O, Or)
+    np.testing.assert_array_equal(L, Lr)
+
+
+def test_decode_varlen_ignores_rows_past_length():
+    """Rows past a sequence's length (here NaN and huge) change nothing, and
+    a sequence equals plain attention over its own keys (SciPy on the
+    explicit score row)."""
+    rng = np.random.default_rng(92)
+    B, H, Lk, D = 4, 2, 50, 8
+    q = rng.standard_normal((B, H, 1, D))
+    k = rng.standard_normal((B, H, Lk, D))
+    v = rng.standard_normal((B, H, Lk, D))
+    lens = [1, 17, 50, 33]
+    k2, v2 = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        k2[b, :, n:] = np.nan
+        v2[b, :, n:] = 1e30
+    O, L = oracle.decode_varlen(q, k2, v2, lens, 0.5)
+    for b, n in enumerate(lens):
+        for h in range(H):
+            a = 0.5 * (k[b, h, :n] @ q[b, h, 0])
+            np.testing.assert_allclose(O[b, h, 0], softmax(a) @ v[b, h, :n], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(L[b, h, 0], logsumexp(a), rtol=1e-13)
+    # length 1: the only value row, the only score
+    np.testing.assert_allclose(O[0, :, 0], v[0, :, 0], rtol=1e-15)
+    np.testing.assert_allclose(L[0, :, 0], 0.5 * np.einsum("hd,hd->h", q[0, :, 0], k[0, :, 0]), rtol=1e-14)
+
+
+def test_decode_varlen_empty_and_clamped_lengths():
+    rng = np.random.default_rng(93)
+    q = rng.standard_normal((3, 1, 1, 8))
+    k = rng.standard_normal((3, 1, 10, 8))
+    v = rng.standard_normal((3, 1, 10, 8))
+    O, L = oracle.decode_varlen(q, k, v, [0, -4, 99], 1.0)
+    assert np.all(O[:2] == 0) and np.all(np.isneginf(L[:2]))
+    Or, Lr = oracle.attention(q[2:], k[2:], v[2:], 1.0)
+    np.testing.assert_array_equal(O[2:], Or)
+    np.testing.assert_array_equal(L[2:], Lr)
