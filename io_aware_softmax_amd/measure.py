@@ -8,6 +8,10 @@ Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
 * ``copy`` - copies a 1 GiB device buffer ``--reps`` times (torch's copy
   kernel): reads and writes exactly 2^30 bytes per launch, the reference
   that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
+* ``sweep_ext`` - shapes past the five workloads: the fp16 sweep at
+  L = 8192, bf16 D128 lengths causal and not, one sequence with one or a few
+  heads (few workgroups), and chunked prefill (Lq new queries against Lk
+  cached keys).  One JSON line per case.
 * ``sweep`` - the fp16 length sweep (B4 H8 D64, L = 64 ... 4096,
   non-causal): TFLOP/s of ``attn_fwd`` next to a materialised-softmax GPU
   baseline that writes the scores and weights to device memory (the naive
@@ -116,16 +120,58 @@ def cmd_sweep(args):
         torch.cuda.empty_cache()
 
 
+def cmd_sweep_ext(args):
+    """Shapes beyond the five workloads: the fp16 sweep at L = 8192, bf16 D = 128
+    lengths, a single sequence and head (few workgroups), and chunked prefill
+    (Lq new queries against Lk cached keys, bottom-right causal)."""
+    cases = [
+        # (label, B, H, Lq, Lk, D, dtype, causal, materialised baseline)
+        ("fp16 sweep extension", 4, 8, 8192, 8192, 64, "f16", False, True),
+        ("bf16 D128 non-causal", 1, 32, 2048, 2048, 128, "bf16", False, False),
+        ("bf16 D128 non-causal", 1, 32, 16384, 16384, 128, "bf16", False, False),
+        ("bf16 D128 causal", 1, 32, 2048, 2048, 128, "bf16", True, False),
+        ("bf16 D128 causal", 1, 32, 16384, 16384, 128, "bf16", True, False),
+        ("single sequence, one head", 1, 1, 16384, 16384, 128, "bf16", True, False),
+        ("single sequence, one head", 1, 1, 65536, 65536, 128, "bf16", True, False),
+        ("single sequence, 8 heads", 1, 8, 16384, 16384, 128, "bf16", True, False),
+        ("chunked prefill", 1, 32, 512, 8192, 128, "bf16", True, False),
+        ("chunked prefill", 1, 32, 2048, 8192, 128, "bf16", True, False),
+    ]
+    for i, (label, B, H, Lq, Lk, D, dt, causal, mat) in enumerate(cases):
+        wl = inputs.custom(f"ext_{i}", B, H, Lq, Lk, D, dt, causal, seed=900 + i)
+        q, k, v = _upload(wl)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, Lq, dtype=torch.float32, device="cuda")
+        scale = 1.0 / math.sqrt(D)
+        # Algorithmic flops: 4 D per allowed (query, key) pair.
+        if causal:
+            off = Lk - Lq
+            pairs = sum(min(Lk, i + off + 1) for i in range(Lq))
+        else:
+            pairs = Lq * Lk
+        flops = 4.0 * B * H * D * pairs
+        ours = _time(lambda: binding.attn_fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse), args.reps)
+        rec = {"case": label, "B": B, "H": H, "Lq": Lq, "Lk": Lk, "D": D, "dtype": dt, "causal": causal,
+               "flops": flops, "attn_fwd_ms": ours[0], "attn_fwd_tflops": flops / ours[0] / 1e9}
+        if mat:
+            base = _time(lambda: _materialised(q, k, v, scale), max(3, args.reps // 4))
+            rec["materialised_ms"] = base[0]
+            rec["speedup"] = base[0] / ours[0]
+        print(json.dumps(rec), flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    p.add_argument("cmd", choices=["kernels", "copy", "sweep"])
+    p.add_argument("cmd", choices=["kernels", "copy", "sweep", "sweep_ext"])
     p.add_argument("--reps", type=int, default=5)
     args = p.parse_args(argv)
     if not torch.cuda.is_available():
         print("needs a GPU", file=sys.stderr)
         return 1
     binding.load()
-    {"kernels": cmd_kernels, "copy": cmd_copy, "sweep": cmd_sweep}[args.cmd](args)
+    {"kernels": cmd_kernels, "copy": cmd_copy, "sweep": cmd_sweep, "sweep_ext": cmd_sweep_ext}[args.cmd](args)
     return 0
 
 

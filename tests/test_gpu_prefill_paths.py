@@ -112,3 +112,29 @@ def test_item_schedules(H, L, causal):
     vals = {t: _normal((B, H, L, D), 800 + i + H) for i, t in enumerate("qkv")}
     say(f"case item schedule H{H} L{L} causal={causal}")
     _check(f"schedule H{H} L{L}", vals, "bf16", causal, 1.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal", [
+    (4, 8, 8192, 8192, 64, "f16", False),      # the fp16 sweep extended to L = 8192
+    (1, 32, 512, 8192, 128, "bf16", True),     # chunked prefill: 512 new queries, 8192 cached keys
+    (1, 32, 2048, 8192, 128, "bf16", True),
+    (1, 1, 65536, 65536, 128, "bf16", True),   # one sequence, one head
+])
+def test_extended_shapes_sampled_rows(B, H, Lq, Lk, D, dtype, causal):
+    """Shapes of the extended sweep, on 64 seeded rows per (b, h) (rows 0 and
+    Lq-1 included)."""
+    import torch
+    from io_aware_softmax_amd import binding
+    wl = inputs.custom(f"ext_{B}x{H}_{Lq}x{Lk}_D{D}", B, H, Lq, Lk, D, dtype, causal, seed=Lq + Lk + D)
+    bits = inputs.generate(wl)
+    q, k, v = (to_device(bits[t], dtype) for t in "qkv")
+    O, L = binding.attn_fwd(q, k, v, causal=causal, scale=wl.scale)
+    torch.cuda.synchronize()
+    O, L = to_host_f64(O), to_host_f64(L)
+    say(f"case extended shape B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal}")
+    for b in range(B):
+        for h in range(H):
+            rows = inputs.sample_rows(wl, h, 64)
+            vals = {t: inputs.slab_values(wl, t, b, h)[None, None] for t in "qkv"}
+            Or, Lr = oracle.attention(vals["q"], vals["k"], vals["v"], wl.scale, causal, rows=rows)
+            compare(f"{wl.name} b{b} h{h}", dtype, O[b, h][rows][None, None], L[b, h][rows][None, None], Or, Lr)
