@@ -16,7 +16,13 @@ the two source pages:
   Safe Softmax" and 6.3.3 "FlashAttention Forward Process" (its "Decoupled
   Softmax", "A Simple Example" and "Full Forward Process" parts).
 
-Pins (in ``tests/test_oracle.py``): the two-block worked example [1,2,3,4],
+``attention_bwd`` is the gradient of ``attention`` with respect to q, k and
+v for an upstream gradient of O (the chapter's note that the training
+backward recomputes instead of storing), written as the plain chain rule.
+
+Pins (in ``tests/test_oracle.py``; the backward's in
+``tests/test_oracle_bwd.py``: finite differences, float64 autograd, closed
+forms, invariants and planted mistakes): the two-block worked example [1,2,3,4],
 closed forms (identical keys, constant values, zero scale, one key, causal
 row 0), invariants (row permutation, key shift), SciPy's ``softmax`` /
 ``logsumexp`` on explicit score matrices, and brute force over every chunk
@@ -25,6 +31,7 @@ partition for L <= 8 across the independent recurrences below.
 
 from .attention import (  # noqa: F401
     attention,
+    attention_bwd,
     decode_varlen,
     one_pass_chunked,
     tiled_outer_kv,

@@ -38,6 +38,7 @@ import numpy as np
 
 __all__ = [
     "attention",
+    "attention_bwd",
     "decode_varlen",
     "two_pass_chunked",
     "one_pass_chunked",
@@ -156,6 +157,96 @@ def decode_varlen(q, k, v, seqlens, scale: float):
             continue
         O[b:b + 1], LSE[b:b + 1] = attention(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], scale)
     return O, LSE
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False, q_rows=None, k_rows=None,
+                  row_block: int = 1024):
+    """Gradients of exact attention with respect to q, k and v, in float64.
+
+    The comfyai.app chapter "6.3 FlashAttention" states (after its "A simple
+    implementation w/ C++" part, and again in "Computation and GPU Memory")
+    that the training backward pass keeps no score or weight matrix from the
+    forward and recomputes what it needs instead, at a cost of the same
+    order as the forward.  The pages give no backward formulas, so this is
+    the plain derivative of the forward's definition (``attention``) for an
+    upstream gradient ``do`` of O, written out with every matrix
+    materialised:
+
+      a  = scale * q k^T, masked entries -inf     (the forward's scores)
+      P  = softmax of each row of a               (the forward's weights)
+      dV = P^T dO
+      dP = dO V^T
+      dA_ij = P_ij (dP_ij - sum_l P_il dP_il)      (Jacobian of the softmax)
+      dQ = scale * dA K,    dK = scale * dA^T Q
+
+    Masked entries have P = 0 and so contribute nothing.  No gradient flows
+    into LSE (it is treated as an output nobody differentiates).
+
+    Args:
+      q, do: [B, H, Lq, D]; k, v: [B, H, Lk, D]; any real float dtypes.
+      scale, causal: as for ``attention``.
+      q_rows: optional query rows whose dQ is returned (all keys are used).
+      k_rows: optional key rows whose dK, dV are returned (all queries are
+        used; every row of the weights is still computed in full).
+      row_block: query rows per materialised block.
+
+    Returns:
+      (dQ [B, H, Rq, D], dK [B, H, Rk, D], dV [B, H, Rk, D]) in float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if do.shape != q.shape or k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+        raise ValueError("q, do must be [B, H, Lq, D]; k, v [B, H, Lk, D]")
+    if causal and Lq > Lk:
+        raise ValueError("causal attention needs Lq <= Lk")
+    q_rows = np.arange(Lq) if q_rows is None else np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.arange(Lk) if k_rows is None else np.asarray(k_rows, dtype=np.int64)
+    dQ = np.zeros((B, H, len(q_rows), D), dtype=np.float64)
+    dK = np.zeros((B, H, len(k_rows), D), dtype=np.float64)
+    dV = np.zeros((B, H, len(k_rows), D), dtype=np.float64)
+    # Query blocks: every row when key gradients are wanted, else the rows asked for.
+    need_all = len(k_rows) > 0
+    for b in range(B):
+        for h in range(H):
+            kk = k[b, h].astype(np.float64)
+            vv = v[b, h].astype(np.float64)
+            blocks = range(0, Lq, row_block) if need_all else range(0, len(q_rows), row_block)
+            for r0 in blocks:
+                rr = np.arange(r0, min(r0 + row_block, Lq)) if need_all else q_rows[r0:r0 + row_block]
+                qq = q[b, h, rr].astype(np.float64)
+                g = do[b, h, rr].astype(np.float64)
+                a = scale * (qq @ kk.T)
+                a = np.where(_allowed_keys(rr, Lq, Lk, causal), a, -np.inf)
+                e = np.exp(a - a.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                da = _softmax_vjp(p, g @ vv.T)
+                dv, dk, dq = _score_grads(p, da, qq, kk, g, scale)
+                dV[b, h] += dv[k_rows]
+                dK[b, h] += dk[k_rows]
+                if need_all:
+                    # Rows of this block that were asked for, in the caller's order.
+                    pos = np.nonzero((q_rows >= rr[0]) & (q_rows <= rr[-1]))[0]
+                    if len(pos):
+                        dQ[b, h, pos] = dq[q_rows[pos] - rr[0]]
+                else:
+                    dQ[b, h, r0:r0 + len(rr)] = dq
+    return dQ, dK, dV
+
+
+def _softmax_vjp(p, dp):
+    """dA_ij = P_ij (dP_ij - sum_l P_il dP_il): the upstream gradient dP of
+    the weights pulled back through each row's softmax."""
+    return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+
+
+def _score_grads(p, da, qq, kk, g, scale):
+    """Products of one query block: P^T dO (values), scale dA^T Q (keys) and
+    scale dA K (queries), the last two from a = scale q k^T."""
+    return p.T @ g, scale * (da.T @ qq), scale * (da @ kk)
 
 
 def _check_block(p, o, m, lse, allowed, vv):
