@@ -1,5 +1,6 @@
 /*
- * attn.h - C ABI of the exact attention forward for AMD MI355X (gfx950).
+ * attn.h - C ABI of the exact attention forward (and its backward) for AMD
+ * MI355X (gfx950).
  *
  * The library computes O = softmax(scale * Q K^T) V for every (batch, head)
  * in one pass over key/value tiles, keeping a running row maximum, a running
@@ -57,7 +58,7 @@ typedef enum {
   ATTN_ERR_NULL = -1,           /* a required pointer is NULL */
   ATTN_ERR_DIM = -2,            /* a dimension <= 0, or a size that overflows the index types */
   ATTN_ERR_UNSUPPORTED_D = -3,  /* head dim D is not 64 or 128 */
-  ATTN_ERR_DTYPE = -4,          /* unknown attn_dtype_t */
+  ATTN_ERR_DTYPE = -4,          /* unknown attn_dtype_t, or one the entry point does not take */
   ATTN_ERR_SCALE = -5,          /* scale is NaN or infinite */
   ATTN_ERR_CAUSAL_SHAPE = -6,   /* causal with Lq > Lk */
   ATTN_ERR_SPLITS = -7,         /* num_splits outside [0, ATTN_MAX_SPLITS] */
@@ -123,6 +124,40 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
 int attn_decode_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            const int* seqlens, int B, int H, int Lk_max, int D, float scale,
                            int num_splits, void* stream, int dtype);
+
+/*
+ * attn_bwd - gradients of attn_fwd's O with respect to q, k and v.
+ *
+ * The comfyai.app chapter "6.3 FlashAttention" notes (after "A simple
+ * implementation w/ C++" and in "Computation and GPU Memory") that for
+ * training the method stores no score or weight matrix and recomputes what
+ * the backward pass needs.  Given the upstream gradient dout = dL/dO, this
+ * call recomputes the weights tile by tile as P_ij = exp(a_ij - lse_i) from
+ * the forward's lse and returns the chain rule of O = softmax(a) V with
+ * a = scale * q k^T (and the same mask):
+ *   dv = P^T dout,  ds = P o (dout v^T - rowsum(dout o o)),
+ *   dq = scale * ds k,  dk = scale * ds^T q.
+ * Nothing of size Lq x Lk is written to device memory.  No gradient flows
+ * into lse.
+ *
+ * q, o, dout, dq are [B,H,Lq,D]; k, v, dk, dv are [B,H,Lk,D] (all `dtype`);
+ * lse is [B,H,Lq] float32.  o and lse must be attn_fwd's outputs for the
+ * same q, k, v, causal and scale (they are trusted, not checked).  dtype is
+ * ATTN_F16 or ATTN_BF16 (ATTN_F32 returns ATTN_ERR_DTYPE); D is 64 or 128.
+ * Products run on MFMA with 16-bit operands (P and ds are rounded to
+ * `dtype`) and fp32 accumulation; the outputs are rounded once to `dtype`.
+ * Every output element has a single writer (no atomics): results are
+ * deterministic.
+ *
+ * The forward's checks apply to q, k, v, o, lse and the sizes; in addition
+ * dout, dq, dk, dv must be non-NULL and 16-byte aligned, and dq, dk, dv must
+ * overlap neither an input nor each other (ATTN_ERR_ALIAS).  Allocates a
+ * stream-ordered workspace of 512 * B * H * ceil(Lq / 64) bytes with
+ * hipMallocAsync on `stream` and releases it on the same stream.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D,
+             int causal, float scale, void* stream, int dtype);
 
 /*
  * attn_decode_auto_splits - the split count attn_fwd and attn_decode_fwd

@@ -22,7 +22,8 @@ LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
-EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_decode_auto_splits", "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_bwd", "attn_decode_auto_splits",
+            "attn_strerror")
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_fwd.restype = i
         lib.attn_decode_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
         lib.attn_decode_varlen_fwd.restype = i
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
+        lib.attn_bwd.restype = i
         lib.attn_decode_auto_splits.argtypes = [i, i, i, i]
         lib.attn_decode_auto_splits.restype = i
         lib.attn_strerror.argtypes = [i]
@@ -165,6 +168,40 @@ def attn_decode_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, se
                                       lse.data_ptr(), seqlens.data_ptr(), B, H, Lk, D, scale,
                                       int(num_splits), _stream_handle(stream), _DTYPE_CODES[q.dtype]))
     return out, lse
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dq, dk, dv of attention through ``attn_bwd``.
+
+    ``out`` and ``lse`` are what ``attn_fwd`` returned for the same q, k, v,
+    causal and scale; ``dout`` is the gradient of the loss with respect to
+    ``out`` (same shape and dtype).  float16 / bfloat16 only.
+    """
+    lib = load()
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    _prep(q, k, v, out, lse, Lq)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a GPU tensor shaped and typed like q")
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    if lse.shape != (B, H, Lq):
+        raise ValueError("lse must be [B, H, Lq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like its input")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
+                        int(bool(causal)), scale, _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return dq, dk, dv
 
 
 def attn_decode_auto_splits(B: int, H: int, Lk: int, D: int) -> int:

@@ -1,5 +1,6 @@
-// C ABI of the attention forward: argument validation, kernel dispatch and
-// the decode workspace.  Declarations and the contract are in include/attn.h.
+// C ABI of the attention forward and backward: argument validation, kernel
+// dispatch and the stream-ordered workspaces.  Declarations and the
+// contract are in include/attn.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -173,6 +174,61 @@ ATTN_EXPORT int attn_decode_varlen_fwd(const void* q, const void* k, const void*
                     static_cast<hipStream_t>(stream), dtype, seqlens);
 }
 
+ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
+                         int D, int causal, float scale, void* stream, int dtype) {
+  if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  // The forward's checks cover q, k, v, o, lse, the sizes, scale and causal.
+  int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if (mis & 15u) return ATTN_ERR_ALIGN;
+  const int64_t BH = int64_t(B) * H;
+  const size_t es = elem_bytes(dtype);
+  const size_t nq = size_t(BH) * Lq * D * es, nk = size_t(BH) * Lk * D * es;
+  const size_t nl = size_t(BH) * Lq * sizeof(float);
+  // Outputs must not overlap any input or each other.
+  const void* in[6] = {q, k, v, o, dout, lse};
+  const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
+  void* out[3] = {dq, dk, dv};
+  const size_t out_n[3] = {nq, nk, nk};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], out_n[i], in[j], in_n[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(out[i], out_n[i], out[j], out_n[j])) return ATTN_ERR_ALIAS;
+  }
+  if (BH * ((int64_t(Lk) + 127) / 128) > kMaxWorkgroups || BH * ((int64_t(Lq) + 63) / 64) > kMaxWorkgroups)
+    return ATTN_ERR_DIM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_workspace_bytes(int(BH), Lq), s);
+  if (e != hipSuccess) return hip_fail(e);
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.stats = static_cast<float*>(ws);
+  a.BH = int(BH);
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.c = scale * attn::kLog2e;
+  a.scale = scale;
+  e = attn::launch_bwd(dtype, D, causal != 0, a, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return ATTN_OK;
+}
+
 ATTN_EXPORT int attn_decode_auto_splits(int B, int H, int Lk, int D) {
   if (B <= 0 || H <= 0 || Lk <= 0 || D <= 0) return ATTN_ERR_DIM;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
@@ -186,7 +242,7 @@ ATTN_EXPORT const char* attn_strerror(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_DIM: return "a dimension is <= 0 or a size exceeds the index range";
     case ATTN_ERR_UNSUPPORTED_D: return "head dimension must be 64 or 128";
-    case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_F32, ATTN_F16 or ATTN_BF16)";
+    case ATTN_ERR_DTYPE: return "unsupported dtype (ATTN_F32, ATTN_F16 or ATTN_BF16; attn_bwd: ATTN_F16 or ATTN_BF16)";
     case ATTN_ERR_SCALE: return "scale is NaN or infinite";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal attention requires Lq <= Lk";
     case ATTN_ERR_SPLITS: return "num_splits must be in [0, ATTN_MAX_SPLITS]";

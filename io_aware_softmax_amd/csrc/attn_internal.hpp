@@ -42,6 +42,24 @@ struct DecodeArgs {
   bool neg;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* stats;  // workspace: per 64-query tile, lse * log2(e) [64] then Dv [64]
+  int BH;
+  int Lq;
+  int Lk;
+  float c;       // scale * log2(e) (signed)
+  float scale;
+};
+
 // Workgroups of `kernel` (block threads, static LDS only) that device `dev`
 // holds resident at once: compute units times workgroups per unit.  Cached.
 hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out);
@@ -52,6 +70,10 @@ hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs&
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
 // The same algorithm with fp32 inputs on the fp32 MFMA.
 hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
+// Attention backward (16-bit dtypes): stats, dK/dV and dQ kernels on stream s.
+hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s);
+// Bytes of BwdArgs::stats for B * H = BH and Lq queries.
+size_t bwd_workspace_bytes(int BH, int Lq);
 // Split-KV decode: partials then combine, both on stream s.
 hipError_t launch_decode(int dtype, int D, const DecodeArgs& a, hipStream_t s);
 

@@ -1,0 +1,507 @@
+// Attention backward (dQ, dK, dV) for fp16 / bf16 on gfx950 MFMA.
+//
+// The comfyai.app chapter "6.3 FlashAttention" notes (after "A simple
+// implementation w/ C++", and in "Computation and GPU Memory") that for
+// training the method keeps no score or weight matrix from the forward and
+// recomputes them in the backward pass.  Here the weights are recomputed
+// tile by tile from the per-row log-sum-exp the forward already writes:
+// P_ij = exp(a_ij - lse_i), so no running maximum is needed.  With
+// Dv_i = sum_d dO_id O_id (which equals sum_j P_ij dP_ij, since O = P V),
+// the chain rule of O = softmax(a) V, a = scale Q K^T gives
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - Dv),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Nothing of size L x L reaches device memory.
+//
+// Three kernels on one stream:
+//   * stats: per 64-query tile, lse in base-2 units and Dv (one pass over
+//     O and dO); padded rows get lse = +inf and Dv = 0, so their weights
+//     and score gradients are exactly zero downstream;
+//   * dK/dV: one workgroup per 128 keys (4 waves x 32 keys held in VGPRs as
+//     MFMA B operands), streaming 64-query tiles of Q, dO and the stats
+//     through LDS by DMA, double buffered; dK and dV accumulate in registers;
+//   * dQ: one workgroup per 128 queries (4 waves x 32 queries, Q and dO in
+//     VGPRs), streaming 64-key tiles of K and V; dQ accumulates in
+//     registers.  No atomics: every output element has one writer, and the
+//     result does not depend on scheduling.
+//
+// Q, dO (dK/dV kernel) and K (dQ kernel) are read from LDS both along rows
+// (A operand of a product over D) and across rows (B operand of a product
+// over the tile's rows, ds_read_b64_tr_b16).  Tiles are stored unpadded with
+// each 16-byte chunk c of row r at chunk c ^ swz(r): both read patterns are
+// then free of bank conflicts (16 lanes reading one chunk of 16 rows hit 16
+// different 4-bank groups; a half-wave's 4 rows x 64 B transposed read hits
+// 64 different banks).
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "attn_internal.hpp"
+#include "mfma_tile.hpp"
+
+namespace attn {
+namespace {
+
+using namespace mt;
+
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int BQ = 64;    // rows per LDS tile (queries for dK/dV, keys for dQ)
+constexpr int BW = 128;   // rows owned by a workgroup (4 waves x 32)
+constexpr int kStatFloats = 2 * BQ;  // per stats tile: lse2[64], then Dv[64]
+
+template <int D>
+struct SwzTile {
+  static constexpr int CPR = D / 8;       // 16-byte chunks per row
+  static constexpr int PITCH = D * 2;     // bytes per row (no padding)
+  static constexpr int BYTES = BQ * PITCH;
+  static constexpr int INST = BYTES / 1024;  // 64-lane DMA instructions per tile
+  static constexpr int PER_WAVE = INST / 4;
+  static_assert(INST % 4 == 0, "tile DMA splits evenly over 4 waves");
+  // Chunk permutation of row r (depends on r mod 16 only).
+  //  D = 128 (one row spans all 64 banks): bits 0-1 of r go to bits 2-3 of
+  //   the chunk, bits 2-3 of r to bits 0-1.  16 consecutive rows: 16
+  //   distinct chunks.  4 consecutive rows (r mod 4 = 0..3): 4 distinct
+  //   4-chunk groups.
+  //  D = 64 (two rows per 64 banks, bit 0 of r picks the half): bit 1 of r
+  //   goes to bit 2 of the chunk, bits 2-3 of r to bits 0-1.
+  __device__ static int swz(int r) {
+    if constexpr (D == 128)
+      return ((r & 3) << 2) | ((r >> 2) & 3);
+    else
+      return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+};
+
+// DMA of one 64-row tile (row 0 at `src`) into swizzled LDS.  Rows at or
+// past rows_left (>= 1) fetch row rows_left - 1 instead (in bounds; their
+// results are discarded or zero-weighted).  `src` must be wave-uniform.
+template <int D>
+__device__ __forceinline__ void dma_swz_tile(const char* src, char* dst, int w, int lane, int rows_left) {
+  using T = SwzTile<D>;
+#pragma unroll
+  for (int i = 0; i < T::PER_WAVE; ++i) {
+    const int inst = w * T::PER_WAVE + i;
+    const int slot = inst * 64 + lane;
+    const int row = slot / T::CPR, pc = slot % T::CPR;
+    const int r = row < rows_left ? row : rows_left - 1;
+    const unsigned off = (unsigned)r * (D * 2) + 16u * (unsigned)(pc ^ T::swz(row));
+    dma_run<1>(src, &off, lds_addr(dst + inst * 1024));
+  }
+}
+
+// One stats tile (512 B) into LDS; lanes 32-63 fetch the same bytes again
+// into the following 512 B (a whole instruction, never read).
+__device__ __forceinline__ void dma_stats(const float* src, char* dst, int lane) {
+  const unsigned off = 16u * (unsigned)(lane & 31);
+  dma_run<1>(reinterpret_cast<const char*>(src), &off, lds_addr(dst));
+}
+
+__device__ __forceinline__ void land_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <bool BF16>
+__device__ __forceinline__ float load16(const unsigned short* p) {
+  const unsigned short b = *p;
+  if constexpr (BF16)
+    return __builtin_bit_cast(float, (unsigned)b << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Bit-permuted row read by lane n for products over D: bits 2 and 3 of n
+// swapped, so that accumulator register r of the 32 x 32 result holds row
+// 16 (r / 8) + 8 h + r % 8 -- the rows of the next product's k-steps.
+__device__ __forceinline__ int perm_row(int n) { return (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1); }
+
+// ---------------------------------------------------------------------------
+// stats: lse2 = lse * log2(e) and Dv = rowsum(dO o O), tile-blocked.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(NT) void bwd_stats_kernel(BwdArgs a) {
+  const int tile = blockIdx.x;  // bh * nqt + t
+  const int nqt = (a.Lq + BQ - 1) / BQ;
+  const int bh = tile / nqt, t = tile % nqt;
+  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int qi = t * BQ + r;
+  float acc = 0.f;
+  if (qi < a.Lq) {
+    const size_t row = ((size_t)bh * a.Lq + qi) * D + part * (D / 4);
+    if constexpr (DT == 0) {
+      const float* o = static_cast<const float*>(a.o) + row;
+      const float* g = static_cast<const float*>(a.dout) + row;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) acc = __builtin_fmaf(o[i], g[i], acc);
+    } else {
+      const unsigned short* o = static_cast<const unsigned short*>(a.o) + row;
+      const unsigned short* g = static_cast<const unsigned short*>(a.dout) + row;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) acc = __builtin_fmaf(load16<DT == 2>(o + i), load16<DT == 2>(g + i), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (part == 0) {
+    float* st = a.stats + (size_t)tile * kStatFloats;
+    st[r] = qi < a.Lq ? a.lse[(size_t)bh * a.Lq + qi] * kLog2e : INFINITY;
+    st[BQ + r] = qi < a.Lq ? acc : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup = 128 keys, loop over 64-query tiles.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16;  // k-steps of a product over D
+  constexpr int DB = D / 32;  // 32-column blocks of D
+  constexpr int STAGE = 2 * T::BYTES + 1024;  // Q tile, dO tile, stats
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int li = lane & 15, g = lane >> 4;
+  const int Lq = a.Lq, Lk = a.Lk;
+  const int off = Lk - Lq;  // bottom-right causal alignment
+  const int nkb = (Lk + BW - 1) / BW;
+  const int nqt = (Lq + BQ - 1) / BQ;
+  // Workgroups are dealt to the 8 XCDs round robin: consecutive key blocks
+  // of one head (which stream the same Q / dO) share an XCD and its L2.
+  // Causal: the first key blocks see the most queries and go first.
+  const int total = a.BH * nkb;
+  const int wg = blockIdx.x;
+  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+  const int bh = logical / nkb, kb = logical % nkb;
+  const int k0 = kb * BW, kw0 = k0 + 32 * w;
+  const int t_begin = CAUSAL ? max(0, k0 - off) / BQ : 0;
+
+  const unsigned short* Kg = static_cast<const unsigned short*>(a.k) + (size_t)bh * Lk * D;
+  const unsigned short* Vg = static_cast<const unsigned short*>(a.v) + (size_t)bh * Lk * D;
+  const char* Qb = static_cast<const char*>(a.q) + (size_t)bh * Lq * D * 2;
+  const char* dOb = static_cast<const char*>(a.dout) + (size_t)bh * Lq * D * 2;
+  const float* Sb = a.stats + (size_t)bh * nqt * kStatFloats;
+
+  auto issue = [&](int t, char* stage) {
+    const int q0 = t * BQ;
+    const int rows_left = min(BQ, Lq - q0);
+    dma_swz_tile<D>(Qb + (size_t)q0 * D * 2, stage, w, lane, rows_left);
+    dma_swz_tile<D>(dOb + (size_t)q0 * D * 2, stage + T::BYTES, w, lane, rows_left);
+    if (w == 0) dma_stats(Sb + (size_t)t * kStatFloats, stage + 2 * T::BYTES, lane);
+  };
+  issue(t_begin, smem);
+
+  // K and V rows of this wave as B operands: lane (n, h) holds
+  // X[kw0 + n][16 t + 8 h .. + 8].  Keys past Lk are zero (never stored).
+  const int key = kw0 + n;
+  s16x8 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+    if (key < Lk) {
+      xk = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + 16 * t + 8 * h);
+      xv = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + 16 * t + 8 * h);
+    }
+    kreg[t] = __builtin_bit_cast(s16x8, xk);
+    vreg[t] = __builtin_bit_cast(s16x8, xv);
+  }
+
+  // Per-lane LDS offsets.  Row reads (A operands over D): row perm_row(n),
+  // chunk 2 t + h.  Transposed reads (B operands over queries): rows
+  // 8 h + li / 4 (+ 4 for the upper half), bytes 64 db + 32 (g & 1) +
+  // 8 (li & 3) of the unswizzled row.
+  const int prow = perm_row(n);
+  unsigned ra[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) ra[t] = prow * T::PITCH + 16 * ((2 * t + h) ^ T::swz(prow));
+  unsigned ta[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * h + (li >> 2) + 4 * hi;
+      const int chunk = 4 * db + 2 * (g & 1) + ((li & 3) >> 1);
+      ta[db][hi] = row * T::PITCH + 16 * (chunk ^ T::swz(row)) + 8 * (li & 1);
+    }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  const float c = a.c;
+
+  // One 32-query block b of the tile in `stage`.
+  auto block = [&](const char* stage, int q0, int b) __attribute__((always_inline)) {
+    const int qb = q0 + 32 * b;
+    if (qb >= Lq) return;
+    if (CAUSAL && qb + 31 + off < kw0) return;  // no query of the block sees a key of the wave
+    const char* Qs = stage;
+    const char* dOs = stage + T::BYTES;
+    const float* st = reinterpret_cast<const float*>(stage + 2 * T::BYTES);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      s = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Qs + 32 * b * T::PITCH + ra[t]), kreg[t], s);
+      dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(dOs + 32 * b * T::PITCH + ra[t]), vreg[t], dp);
+    }
+    // Register r holds query qb + 16 (r / 8) + 8 h + r % 8 of key kw0 + n.
+    float l2[16], dd[16];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int base = 32 * b + 16 * hh + 8 * h;
+      *reinterpret_cast<float4*>(l2 + 8 * hh) = *reinterpret_cast<const float4*>(st + base);
+      *reinterpret_cast<float4*>(l2 + 8 * hh + 4) = *reinterpret_cast<const float4*>(st + base + 4);
+      *reinterpret_cast<float4*>(dd + 8 * hh) = *reinterpret_cast<const float4*>(st + BQ + base);
+      *reinterpret_cast<float4*>(dd + 8 * hh + 4) = *reinterpret_cast<const float4*>(st + BQ + base + 4);
+    }
+    const bool masked = CAUSAL && qb + off < kw0 + 31;
+    s16x8 pa[2], sa[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
+      if (masked) {
+        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+        if (key > qi + off) p = 0.f;
+      }
+      const float ds = p * (dp[r] - dd[r]);
+      pa[r >> 3][r & 7] = (short)round16<BF16>(p);
+      sa[r >> 3][r & 7] = (short)round16<BF16>(ds);
+    }
+    // dV += P^T dO and dK += dS^T Q over the block's 32 queries (2 k-steps).
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int rowoff = (32 * b + 16 * s2) * T::PITCH;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 glo = lds_read_tr(dOs + rowoff + ta[db][0]);
+        const s16x4 ghi = lds_read_tr(dOs + rowoff + ta[db][1]);
+        const s16x4 qlo = lds_read_tr(Qs + rowoff + ta[db][0]);
+        const s16x4 qhi = lds_read_tr(Qs + rowoff + ta[db][1]);
+        const s16x8 gf = s16x8{glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
+        const s16x8 qf = s16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+        dv[db] = mfma32<BF16>(pa[s2], gf, dv[db]);
+        dk[db] = mfma32<BF16>(sa[s2], qf, dk[db]);
+      }
+    }
+  };
+
+  land_all();
+  __syncthreads();
+  // Tiles alternate between the two stages; the loop body covers a pair so
+  // that every LDS address is a lane offset plus an immediate.
+  for (int t = t_begin; t < nqt; t += 2) {
+    if (t + 1 < nqt) issue(t + 1, smem + STAGE);
+    block(smem, t * BQ, 0);
+    block(smem, t * BQ, 1);
+    land_all();
+    __syncthreads();
+    if (t + 1 >= nqt) break;
+    if (t + 2 < nqt) issue(t + 2, smem);
+    block(smem + STAGE, (t + 1) * BQ, 0);
+    block(smem + STAGE, (t + 1) * BQ, 1);
+    land_all();
+    __syncthreads();
+  }
+
+  // Register r of block db holds key kw0 + 8 (r / 4) + 4 h + r % 4,
+  // column 32 db + n.
+  unsigned short* dKg = static_cast<unsigned short*>(a.dk) + (size_t)bh * Lk * D;
+  unsigned short* dVg = static_cast<unsigned short*>(a.dv) + (size_t)bh * Lk * D;
+  const float scale = a.scale;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (kr < Lk) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dKg[(size_t)kr * D + 32 * db + n] = round16<BF16>(dk[db][r] * scale);
+        dVg[(size_t)kr * D + 32 * db + n] = round16<BF16>(dv[db][r]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: workgroup = 128 queries, loop over 64-key tiles.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int STAGE = 2 * T::BYTES;  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int li = lane & 15, g = lane >> 4;
+  const int Lq = a.Lq, Lk = a.Lk;
+  const int off = Lk - Lq;
+  const int nqb = (Lq + BW - 1) / BW;
+  const int nqt = (Lq + BQ - 1) / BQ;
+  // Consecutive query blocks of one head share an XCD (same K / V);
+  // causal: the last query blocks (the most keys) go first.
+  const int total = a.BH * nqb;
+  const int wg = blockIdx.x;
+  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+  const int bh = logical / nqb;
+  const int qblk = CAUSAL ? nqb - 1 - logical % nqb : logical % nqb;
+  const int q0 = qblk * BW, wq0 = q0 + 32 * w;
+  const int q_last = min(q0 + BW, Lq) - 1;
+  const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
+  const int nkt = (kv_end + BQ - 1) / BQ;
+  // Keys this wave needs: [0, w_key_end).
+  const int w_key_end = wq0 >= Lq ? 0 : (CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk);
+
+  const char* Kb = static_cast<const char*>(a.k) + (size_t)bh * Lk * D * 2;
+  const char* Vb = static_cast<const char*>(a.v) + (size_t)bh * Lk * D * 2;
+  auto issue = [&](int j, char* stage) {
+    const int kv0 = j * BQ;
+    const int rows_left = min(BQ, Lk - kv0);
+    dma_swz_tile<D>(Kb + (size_t)kv0 * D * 2, stage, w, lane, rows_left);
+    dma_swz_tile<D>(Vb + (size_t)kv0 * D * 2, stage + T::BYTES, w, lane, rows_left);
+  };
+  issue(0, smem);
+
+  // Q and dO rows of this wave as B operands: lane (n, h) holds
+  // X[wq0 + n][16 t + 8 h .. + 8]; the lane's lse2 and Dv.
+  const int qi = wq0 + n;
+  const unsigned short* Qg = static_cast<const unsigned short*>(a.q) + (size_t)bh * Lq * D;
+  const unsigned short* dOg = static_cast<const unsigned short*>(a.dout) + (size_t)bh * Lq * D;
+  s16x8 qreg[KS], oreg[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    u32x4 xq = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
+    if (qi < Lq) {
+      xq = *reinterpret_cast<const u32x4*>(Qg + (size_t)qi * D + 16 * t + 8 * h);
+      xo = *reinterpret_cast<const u32x4*>(dOg + (size_t)qi * D + 16 * t + 8 * h);
+    }
+    qreg[t] = __builtin_bit_cast(s16x8, xq);
+    oreg[t] = __builtin_bit_cast(s16x8, xo);
+  }
+  float l2 = INFINITY, dd = 0.f;
+  if (qi < Lq) {
+    const float* st = a.stats + ((size_t)bh * nqt + qi / BQ) * kStatFloats;
+    l2 = st[qi % BQ];
+    dd = st[BQ + qi % BQ];
+  }
+
+  const int prow = perm_row(n);
+  unsigned ra[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) ra[t] = prow * T::PITCH + 16 * ((2 * t + h) ^ T::swz(prow));
+  unsigned ta[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * h + (li >> 2) + 4 * hi;
+      const int chunk = 4 * db + 2 * (g & 1) + ((li & 3) >> 1);
+      ta[db][hi] = row * T::PITCH + 16 * (chunk ^ T::swz(row)) + 8 * (li & 1);
+    }
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  const float c = a.c;
+
+  // One 32-key block b of the tile in `stage`.
+  auto block = [&](const char* stage, int kv0, int b) __attribute__((always_inline)) {
+    const int kb0 = kv0 + 32 * b;
+    if (kb0 >= w_key_end) return;
+    const char* Ks = stage;
+    const char* Vs = stage + T::BYTES;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      s = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s);
+      dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp);
+    }
+    // Register r holds key kb0 + 16 (r / 8) + 8 h + r % 8 of query qi.
+    const bool masked = kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off);
+    s16x8 sa[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+      if (masked) {
+        const int kj = kb0 + 16 * (r >> 3) + 8 * h + (r & 7);
+        if (kj >= Lk || (CAUSAL && kj > qi + off)) p = 0.f;
+      }
+      sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dp[r] - dd));
+    }
+    // dQ += dS K over the block's 32 keys (2 k-steps).
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int rowoff = (32 * b + 16 * s2) * T::PITCH;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 lo = lds_read_tr(Ks + rowoff + ta[db][0]);
+        const s16x4 hi = lds_read_tr(Ks + rowoff + ta[db][1]);
+        dq[db] = mfma32<BF16>(sa[s2], s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, dq[db]);
+      }
+    }
+  };
+
+  land_all();
+  __syncthreads();
+  for (int j = 0; j < nkt; j += 2) {
+    if (j + 1 < nkt) issue(j + 1, smem + STAGE);
+    block(smem, j * BQ, 0);
+    block(smem, j * BQ, 1);
+    land_all();
+    __syncthreads();
+    if (j + 1 >= nkt) break;
+    if (j + 2 < nkt) issue(j + 2, smem);
+    block(smem + STAGE, (j + 1) * BQ, 0);
+    block(smem + STAGE, (j + 1) * BQ, 1);
+    land_all();
+    __syncthreads();
+  }
+
+  // Register r of block db holds query wq0 + 8 (r / 4) + 4 h + r % 4,
+  // column 32 db + n.
+  unsigned short* dQg = static_cast<unsigned short*>(a.dq) + (size_t)bh * Lq * D;
+  const float scale = a.scale;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qr = wq0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (qr < Lq) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dQg[(size_t)qr * D + 32 * db + n] = round16<BF16>(dq[db][r] * scale);
+    }
+  }
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+  const int nqt = (a.Lq + BQ - 1) / BQ;
+  bwd_stats_kernel<DT, D><<<dim3(a.BH * nqt), dim3(NT), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (a.Lk + BW - 1) / BW;
+  const int nqb = (a.Lq + BW - 1) / BW;
+  bwd_dkdv_kernel<DT == 2, D, CAUSAL><<<dim3(a.BH * nkb), dim3(NT), 0, s>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_dq_kernel<DT == 2, D, CAUSAL><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int BH, int Lq) {
+  return (size_t)BH * ((Lq + BQ - 1) / BQ) * kStatFloats * sizeof(float);
+}
+
+hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s) {
+  if (dtype == 2) {
+    if (D == 128) return causal ? launch_typed<2, 128, true>(a, s) : launch_typed<2, 128, false>(a, s);
+    return causal ? launch_typed<2, 64, true>(a, s) : launch_typed<2, 64, false>(a, s);
+  }
+  if (D == 128) return causal ? launch_typed<1, 128, true>(a, s) : launch_typed<1, 128, false>(a, s);
+  return causal ? launch_typed<1, 64, true>(a, s) : launch_typed<1, 64, false>(a, s);
+}
+
+}  // namespace attn

@@ -6,7 +6,7 @@ HIP path receive what it produces.
 
 Every [L, D] slab of q, k or v for one (batch, head) has its own PCG64 stream
 seeded by ``SeedSequence([*seed_words, tensor_id, b, h])`` (tensor ids q=0,
-k=1, v=2), so any slab can be regenerated alone and slabs can be drawn in
+k=1, v=2, and do=3 for the upstream gradient of O fed to the backward), so any slab can be regenerated alone and slabs can be drawn in
 parallel threads with identical results.  Values are ``standard_normal`` in
 float32, optionally multiplied by a power of two per head (exact, so it
 commutes with rounding), then rounded to nearest-even into the storage type.
@@ -26,7 +26,7 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
 DTYPES = ("f32", "f16", "bf16")
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -98,7 +98,7 @@ class Workload:
         return dict(self.q_head_mult).get(h, 1.0)
 
     def shape(self, tensor: str) -> Tuple[int, int, int, int]:
-        L = self.Lq if tensor == "q" else self.Lk
+        L = self.Lq if tensor in ("q", "do") else self.Lk
         return (self.B, self.H, L, self.D)
 
     def flops(self) -> float:

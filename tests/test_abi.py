@@ -106,6 +106,34 @@ def test_validation_errors(lib):
     assert r(G, 2 * G, 3 * G, 4 * G, 5 * G, 5 * G, 2, 3, 100, 64, 0.1, 0, None, 2) == e["ATTN_ERR_ALIAS"]
 
 
+def _bwd(lib, q=G, k=2 * G, v=3 * G, o=4 * G, do=5 * G, lse=6 * G, dq=7 * G, dk=8 * G, dv=9 * G,
+         B=2, H=3, Lq=16, Lk=16, D=64, causal=0, scale=0.125, dtype=2):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Lq, Lk, D, causal, scale, None, dtype)
+
+
+def test_backward_validation_errors(lib):
+    e = {n: _header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_DIM", "ATTN_ERR_UNSUPPORTED_D",
+                                       "ATTN_ERR_DTYPE", "ATTN_ERR_SCALE", "ATTN_ERR_CAUSAL_SHAPE",
+                                       "ATTN_ERR_ALIAS", "ATTN_ERR_ALIGN")}
+    for kw in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert _bwd(lib, **{kw: 0}) == e["ATTN_ERR_NULL"]
+    for kw in ("B", "H", "Lq", "Lk", "D"):
+        assert _bwd(lib, **{kw: 0}) == e["ATTN_ERR_DIM"]
+    assert _bwd(lib, D=96) == e["ATTN_ERR_UNSUPPORTED_D"]
+    for dt in (0, -1, 3):  # fp32 has no backward
+        assert _bwd(lib, dtype=dt) == e["ATTN_ERR_DTYPE"]
+    assert _bwd(lib, scale=float("nan")) == e["ATTN_ERR_SCALE"]
+    assert _bwd(lib, causal=1, Lq=20, Lk=16) == e["ATTN_ERR_CAUSAL_SHAPE"]
+    base = {"q": G, "k": 2 * G, "v": 3 * G, "o": 4 * G, "do": 5 * G, "lse": 6 * G}
+    for out in ("dq", "dk", "dv"):
+        for name, addr in base.items():
+            assert _bwd(lib, **{out: addr + 64}) == e["ATTN_ERR_ALIAS"], (out, name)
+    assert _bwd(lib, dk=7 * G + 32) == e["ATTN_ERR_ALIAS"]   # dk inside dq
+    assert _bwd(lib, dv=8 * G) == e["ATTN_ERR_ALIAS"]        # dv == dk
+    for kw in ("do", "dq", "dk", "dv"):
+        assert _bwd(lib, **{kw: {"do": 5 * G, "dq": 7 * G, "dk": 8 * G, "dv": 9 * G}[kw] + 8}) == e["ATTN_ERR_ALIGN"]
+
+
 def test_strerror_and_auto_splits(lib):
     for code in range(-10, 1):
         msg = binding.attn_strerror(code)
