@@ -12,7 +12,9 @@ figures.
 Prints ONE JSON line.  ``value`` is the prefill throughput in TFLOP/s
 (4 B H Lq Lk D flops, halved for causal, over the prefill's own average
 duration); the decode throughput (K+V bytes over the decode call's average
-duration) is reported under ``decode``.  ``cpu_baseline`` times the float64
+duration) is reported under ``decode``; the backward of the prefill
+workload (dQ, dK, dV through ``attn_bwd``, timed on its own) under
+``backward``.  ``cpu_baseline`` times the float64
 CPU oracle on a bounded sample of the prefill workload (test infrastructure,
 never part of the timed path).
 """
@@ -45,8 +47,9 @@ def _parse():
     # settle; the default warm-up (about 100 ms) reaches that state first.
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--splits", type=int, default=0, help="decode split count (0 = library choice)")
-    p.add_argument("--parts", default="prefill,decode",
-                   help="comma-separated parts of the step to run (prefill, decode)")
+    p.add_argument("--parts", default="prefill,decode,backward",
+                   help="comma-separated parts to run: prefill and decode (the step), backward "
+                        "(timed on its own, reported under 'backward')")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=24, help="heads of the prefill workload the oracle times")
     return p.parse_args()
@@ -124,15 +127,16 @@ def main():
     wp = inputs.WORKLOADS[PREFILL]
     wd = inputs.WORKLOADS[DECODE]
     parts = {x.strip() for x in args.parts.split(",") if x.strip()}
-    if not parts or parts - {"prefill", "decode"}:
-        print("--parts takes prefill and/or decode", file=sys.stderr)
+    if not parts or parts - {"prefill", "decode", "backward"}:
+        print("--parts takes prefill, decode and/or backward", file=sys.stderr)
         sys.exit(2)
-    run_p, run_d = "prefill" in parts, "decode" in parts
+    run_p, run_d, run_b = "prefill" in parts, "decode" in parts, "backward" in parts
 
     t_gen = time.perf_counter()
-    if run_p:
-        bp = inputs.generate(wp)
+    if run_p or run_b:
+        bp = inputs.generate(wp, ("q", "k", "v", "do") if run_b else ("q", "k", "v"))
         qp, kp, vp = (_to_device(bp[t], wp.dtype) for t in "qkv")
+        gp = _to_device(bp["do"], wp.dtype) if run_b else None
         del bp
         op = torch.empty_like(qp)
         lp = torch.empty(wp.B, wp.H, wp.Lq, dtype=torch.float32, device="cuda")
@@ -241,6 +245,34 @@ def main():
                                 "value": v_bytes / (v_ms * 1e-3) / 1e9, "unit": "GB/s", "ms": v_ms,
                                 "bytes": v_bytes, "lengths": "seeded uniform in [1, 32768] per sequence",
                                 "frac_of_hbm_peak": v_bytes / (v_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if run_b:
+        # Not part of the step: the backward (dQ, dK, dV) of the prefill
+        # workload from the forward's O and LSE and a seeded upstream
+        # gradient.  Flops: the five L x L x D products of the chain rule
+        # (recomputed scores, dP, dV, dK, dQ), 2 flops per multiply-add,
+        # halved for causal.
+        binding.attn_fwd(qp, kp, vp, causal=wp.causal, scale=wp.scale, out=op, lse=lp)
+        dq, dk, dv = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+
+        def bwd():
+            binding.attn_bwd(qp, kp, vp, op, lp, gp, causal=wp.causal, scale=wp.scale, dq=dq, dk=dk, dv=dv)
+
+        for _ in range(10):
+            bwd()
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in bev:
+            a.record(stream)
+            bwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        b_ms = float(np.mean([a.elapsed_time(b) for a, b in bev]))
+        b_flops = 2.5 * wp.flops()
+        rec["backward"] = {"metric": "attention bwd TFLOP/s (causal bf16 B1 H32 L8192 D128, whole attn_bwd call)",
+                           "value": b_flops / (b_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms": b_ms,
+                           "ms_min": float(np.min([a.elapsed_time(b) for a, b in bev])), "flops": b_flops,
+                           "frac_of_mfma_peak": b_flops / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "kernels": "bwd_stats_kernel + bwd_dkdv_kernel + bwd_dq_kernel"}
     rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
                      "arch": getattr(props, "gcnArchName", "")}
     rec["input_gen_s"] = gen_s

@@ -35,6 +35,7 @@
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 #include "attn_internal.hpp"
 #include "mfma_tile.hpp"
@@ -149,6 +150,118 @@ __global__ __launch_bounds__(NT) void bwd_stats_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = 128 keys, loop over 64-query tiles.
 // ---------------------------------------------------------------------------
+
+// One whole, unmasked 64-query tile of a wave as a fixed sequence of MFMA
+// slots (one wave per SIMD, so the overlap of matrix and vector work has to
+// be in the instruction order):
+//   slots [0, NS)          S_0 = Q_0 K^T and dP_0 = dO_0 V^T (block 0)
+//   slots [NS, 2 NS)       S_1, dP_1, while the VALU turns S_0, dP_0 into
+//                          P_0 and dS_0 (two row elements per slot)
+//   slots [2 NS, 2NS + NG) dV += P_0^T dO_0, dK += dS_0^T Q_0, while the
+//                          VALU turns block 1 into P_1, dS_1
+//   slots [2NS + NG, N)    dV += P_1^T dO_1, dK += dS_1^T Q_1
+// Each slot issues its MFMA, its VALU share, the LDS reads of the slot PF
+// ahead and (through `hook`) now and then one DMA instruction of the next
+// tile; a scheduling fence keeps the slots in this order.
+template <int D>
+struct BwdSlots {
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int NS = 2 * KS;       // S and dP MFMAs of one block
+  static constexpr int NG = 4 * DB;       // dV and dK MFMAs of one block
+  static constexpr int N = 2 * NS + 2 * NG;
+  static constexpr int PF = 4;            // read lookahead in slots
+  // Elements go in pairs (one packed conversion each), pair k of block b at
+  // slot E_b + k, one slot after the block's last S / dP product.
+  static constexpr int E0 = NS + 1;
+  static constexpr int E1 = 2 * NS + 1;
+  static constexpr int PFS = 3;           // stats read lookahead in slots
+  // Pairs 0-3 (elements 0-7) feed a block's first dV/dK k-step, pairs 4-7
+  // the second; each must be ready before that k-step's first slot.
+  static_assert(E0 + 3 < 2 * NS && E0 + 7 < 2 * NS + NG / 2, "block 0 elements late");
+  static_assert(E1 + 3 < 2 * NS + NG && E1 + 7 < 2 * NS + NG + NG / 2, "block 1 elements late");
+};
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled.
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+template <bool BF16, int D, class Hook>
+__device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, const float* st,
+                                               const s16x8 (&kreg)[D / 16], const s16x8 (&vreg)[D / 16],
+                                               f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                               const unsigned (&ra)[D / 16], const unsigned (&ta)[D / 32][2],
+                                               int h, float c, Hook&& hook) {
+  using T = SwzTile<D>;
+  using S = BwdSlots<D>;
+  s16x8 fr[S::N];
+  f32x16 sc[2], dp[2];
+  float2 l2[2][8], dd[2][8];  // stats of element pair k, read PFS slots ahead
+  s16x8 pa[2][2], sa[2][2];
+  auto read = [&](int i) __attribute__((always_inline)) {
+    if (i < 2 * S::NS) {
+      const int b = i / S::NS, j = i % S::NS;
+      fr[i] = *reinterpret_cast<const s16x8*>(((j & 1) ? dOs : Qs) + 32 * b * T::PITCH + ra[j >> 1]);
+    } else {
+      const int x = i - 2 * S::NS, b = x / S::NG, j = x % S::NG;
+      const int s2 = j / (2 * S::DB), r = j % (2 * S::DB), db = r >> 1;
+      const char* src = ((r & 1) ? Qs : dOs) + (32 * b + 16 * s2) * T::PITCH;
+      const s16x4 lo = lds_read_tr(src + ta[db][0]);
+      const s16x4 hi = lds_read_tr(src + ta[db][1]);
+      fr[i] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // Elements 2k, 2k+1 of block b are queries 32 b + 16 (k / 4) + 8 h +
+  // 2 (k % 4) + {0, 1} (consecutive: one 8-byte read each of lse2 and Dv).
+  auto stats = [&](int b, int k) __attribute__((always_inline)) {
+    const int q = 32 * b + 16 * (k >> 2) + 8 * h + 2 * (k & 3);
+    l2[b][k] = *reinterpret_cast<const float2*>(st + q);
+    dd[b][k] = *reinterpret_cast<const float2*>(st + BQ + q);
+  };
+  auto pair = [&](int b, int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 2 * k + u;
+      const float lse2 = u ? l2[b][k].y : l2[b][k].x;
+      const float dv_i = u ? dd[b][k].y : dd[b][k].x;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][e], c, -lse2));
+      pa[b][e >> 3][e & 7] = (short)round16<BF16>(p);
+      sa[b][e >> 3][e & 7] = (short)round16<BF16>(p * (dp[b][e] - dv_i));
+    }
+  };
+  static_for<S::PF>([&](auto I) __attribute__((always_inline)) { read(I); });
+  __builtin_amdgcn_sched_barrier(0);
+  static_for<S::N>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    if (i + S::PF < S::N) read(i + S::PF);
+    if (i + S::PFS >= S::E0 && i + S::PFS < S::E0 + 8) stats(0, i + S::PFS - S::E0);
+    if (i + S::PFS >= S::E1 && i + S::PFS < S::E1 + 8) stats(1, i + S::PFS - S::E1);
+    if (i < 2 * S::NS) {
+      const int b = i / S::NS, j = i % S::NS, t = j >> 1;
+      if (j & 1)
+        dp[b] = mfma32<BF16>(fr[i], vreg[t], t == 0 ? f32x16{} : dp[b]);
+      else
+        sc[b] = mfma32<BF16>(fr[i], kreg[t], t == 0 ? f32x16{} : sc[b]);
+    } else {
+      const int x = i - 2 * S::NS, b = x / S::NG, j = x % S::NG;
+      const int s2 = j / (2 * S::DB), r = j % (2 * S::DB), db = r >> 1;
+      if (r & 1)
+        dk[db] = mfma32<BF16>(sa[b][s2], fr[i], dk[db]);
+      else
+        dv[db] = mfma32<BF16>(pa[b][s2], fr[i], dv[db]);
+    }
+    if (i >= S::E0 && i < S::E0 + 8) pair(0, i - S::E0);
+    if (i >= S::E1 && i < S::E1 + 8) pair(1, i - S::E1);
+    hook(I);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using T = SwzTile<D>;
@@ -286,20 +399,71 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // Per-lane source offsets of this wave's DMA instructions for a whole tile.
+  unsigned doff[T::PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::PER_WAVE; ++i) {
+    const int slot = (w * T::PER_WAVE + i) * 64 + lane;
+    const int row = slot / T::CPR;
+    doff[i] = (unsigned)row * (D * 2) + 16u * (unsigned)((slot % T::CPR) ^ T::swz(row));
+  }
+
+  // A whole tile (64 queries before Lq) whose first query sees every key of
+  // the wave takes the slot schedule, with the next tile's DMA spread over
+  // its first slots (Q, then dO, then the stats); on the last tile the DMA
+  // fetches the current tile again into the idle stage (never read).  Other
+  // tiles (causal diagonal, Lq tail) issue the next tile's DMA first and go
+  // block by block.
+  auto tile = [&](char* stage, int q0, char* nstage, int tn) __attribute__((always_inline)) {
+    const bool has_next = tn < nqt;
+    if (q0 + BQ <= Lq && (!CAUSAL || q0 + off >= kw0 + 31)) {
+      const int tf = has_next ? tn : tn - 1;
+      const int rows_left = min(BQ, Lq - tf * BQ);
+      unsigned cur[T::PER_WAVE];
+      if (rows_left == BQ) {
+#pragma unroll
+        for (int i = 0; i < T::PER_WAVE; ++i) cur[i] = doff[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < T::PER_WAVE; ++i) {
+          const int slot = (w * T::PER_WAVE + i) * 64 + lane;
+          const int row = slot / T::CPR;
+          cur[i] = (unsigned)min(row, rows_left - 1) * (D * 2) + 16u * (unsigned)((slot % T::CPR) ^ T::swz(row));
+        }
+      }
+      const char* qsrc = Qb + (size_t)tf * BQ * D * 2;
+      const char* gsrc = dOb + (size_t)tf * BQ * D * 2;
+      const float* ssrc = Sb + (size_t)tf * kStatFloats;
+      auto hook = [&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        constexpr int k = (i - 1) / 2;  // DMA instruction k at slot 2 k + 1
+        if constexpr (i % 2 == 1 && k < T::PER_WAVE) {
+          dma_run<1>(qsrc, &cur[k], lds_addr(nstage + (w * T::PER_WAVE + k) * 1024));
+        } else if constexpr (i % 2 == 1 && k < 2 * T::PER_WAVE) {
+          dma_run<1>(gsrc, &cur[k - T::PER_WAVE], lds_addr(nstage + T::BYTES + (w * T::PER_WAVE + k - T::PER_WAVE) * 1024));
+        } else if constexpr (i % 2 == 1 && k == 2 * T::PER_WAVE) {
+          if (w == 0) dma_stats(ssrc, nstage + 2 * T::BYTES, lane);
+        }
+      };
+      dkdv_tile_fast<BF16, D>(stage, stage + T::BYTES, reinterpret_cast<const float*>(stage + 2 * T::BYTES), kreg,
+                              vreg, dk, dv, ra, ta, h, c, hook);
+    } else {
+      if (has_next) issue(tn, nstage);
+      block(stage, q0, 0);
+      block(stage, q0, 1);
+    }
+  };
+
   land_all();
   __syncthreads();
   // Tiles alternate between the two stages; the loop body covers a pair so
   // that every LDS address is a lane offset plus an immediate.
   for (int t = t_begin; t < nqt; t += 2) {
-    if (t + 1 < nqt) issue(t + 1, smem + STAGE);
-    block(smem, t * BQ, 0);
-    block(smem, t * BQ, 1);
+    tile(smem, t * BQ, smem + STAGE, t + 1);
     land_all();
     __syncthreads();
     if (t + 1 >= nqt) break;
-    if (t + 2 < nqt) issue(t + 2, smem);
-    block(smem + STAGE, (t + 1) * BQ, 0);
-    block(smem + STAGE, (t + 1) * BQ, 1);
+    tile(smem + STAGE, (t + 1) * BQ, smem, t + 2);
     land_all();
     __syncthreads();
   }

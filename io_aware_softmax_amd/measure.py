@@ -4,6 +4,7 @@ Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
 
 * ``kernels`` - uploads the causal bf16 prefill (B1 H32 L8192 D128) and the
   bf16 decode (B16 H32 Lk32768 D128) inputs and runs each kernel call
+  (prefill forward, its backward with a seeded upstream gradient, decode)
   ``--reps`` times, for rocprofv3 kernel traces and counter passes.
 * ``copy`` - copies a 1 GiB device buffer ``--reps`` times (torch's copy
   kernel): reads and writes exactly 2^30 bytes per launch, the reference
@@ -54,9 +55,14 @@ def cmd_kernels(args):
     q, k, v = _upload(wp)
     print(f"prefill {wp.name}: {args.reps} launches", flush=True)
     for _ in range(args.reps):
-        binding.attn_fwd(q, k, v, causal=True, scale=wp.scale)
+        O, L = binding.attn_fwd(q, k, v, causal=True, scale=wp.scale)
     torch.cuda.synchronize()
-    del q, k, v
+    g = _dev(inputs.generate(wp, ("do",))["do"], wp.dtype)
+    print(f"backward {wp.name}: {args.reps} launches", flush=True)
+    for _ in range(args.reps):
+        binding.attn_bwd(q, k, v, O, L, g, causal=True, scale=wp.scale)
+    torch.cuda.synchronize()
+    del q, k, v, O, L, g
     torch.cuda.empty_cache()
     q, k, v = _upload(wd)
     splits = binding.attn_decode_auto_splits(wd.B, wd.H, wd.Lk, wd.D)
