@@ -20,7 +20,13 @@ the two source pages:
 v for an upstream gradient of O (the chapter's note that the training
 backward recomputes instead of storing), written as the plain chain rule.
 
-Pins (in ``tests/test_oracle.py``; the backward's in
+``attention_ex`` / ``attention_ex_bwd`` add a general mask (boolean or
+additive) and dropout on the weights, with the keep pattern drawn from the
+counter-based generator in ``philox.py`` (Philox4x32-10 from its published
+definition).
+
+Pins (in ``tests/test_oracle.py``; the masked / dropout ones in
+``tests/test_oracle_ex.py``; the backward's in
 ``tests/test_oracle_bwd.py``: finite differences, float64 autograd, closed
 forms, invariants and planted mistakes): the two-block worked example [1,2,3,4],
 closed forms (identical keys, constant values, zero scale, one key, causal
@@ -32,6 +38,8 @@ partition for L <= 8 across the independent recurrences below.
 from .attention import (  # noqa: F401
     attention,
     attention_bwd,
+    attention_ex,
+    attention_ex_bwd,
     decode_varlen,
     one_pass_chunked,
     tiled_outer_kv,

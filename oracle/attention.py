@@ -39,6 +39,8 @@ import numpy as np
 __all__ = [
     "attention",
     "attention_bwd",
+    "attention_ex",
+    "attention_ex_bwd",
     "decode_varlen",
     "two_pass_chunked",
     "one_pass_chunked",
@@ -234,6 +236,141 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool = False, q_rows=None, 
                         dQ[b, h, pos] = dq[q_rows[pos] - rr[0]]
                 else:
                     dQ[b, h, r0:r0 + len(rr)] = dq
+    return dQ, dK, dV
+
+
+def _mask_block(mask, mask_kind, b, h, rr, Lk):
+    """Rows rr of the (b, h) slab of a [Bm, Hm, Lq, Lk] mask broadcast over
+    batch and heads of size 1: (allowed bool block, additive float64 block)."""
+    mb = mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0][rr]
+    if mask_kind == "bool":
+        return mb != 0, np.zeros((len(rr), Lk))
+    if mask_kind == "add":
+        add = mb.astype(np.float64)
+        return ~np.isneginf(add), np.where(np.isneginf(add), 0.0, add)
+    raise ValueError("mask_kind is 'bool' or 'add'")
+
+
+def attention_ex(q, k, v, scale: float, causal: bool = False, mask=None, mask_kind=None,
+                 dropout_p: float = 0.0, seed: int = 0, offset: int = 0, rows=None, row_block: int = 1024):
+    """Attention with a general mask and dropout on the weights, float64.
+
+    The fused tile of the comfyai.app chapter "6.3 FlashAttention"
+    (section 6.3.3, "Kernel Fusion") runs scores, scale, mask, softmax,
+    dropout and the value product in one place.  Written out plainly:
+
+      a_ij = scale q_i . k_j (+ mask_ij for an additive mask)
+      keys with a false boolean mask, an additive -inf or (causal) past the
+      bottom-right diagonal are excluded: they drop out of the maximum and
+      the sum;
+      P = softmax of each row over the remaining keys; LSE = m + ln(s) as
+      for ``attention`` (dropout does not change it);
+      O = (P o Z / (1 - p)) V with Z the keep pattern of
+      ``philox.keep_pattern`` (all ones when p = 0).
+    A row with no remaining key has O = 0 and LSE = -inf.
+
+    Args:
+      mask: None, or [Bm, Hm, Lq, Lk] with Bm in {1, B}, Hm in {1, H}
+        (size-1 axes broadcast); mask_kind "bool" (nonzero = attend) or
+        "add" (float values added to the scaled scores, -inf = excluded).
+      dropout_p, seed, offset: dropout probability (float32 value used) and
+        the generator's key and counter word.
+      rows, row_block: as for ``attention``.
+    Returns:
+      (O [B, H, R, D], LSE [B, H, R]) in float64.
+    """
+    from .philox import keep_pattern
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if causal and Lq > Lk:
+        raise ValueError("causal attention needs Lq <= Lk")
+    if mask is not None:
+        mask = np.asarray(mask)
+        if mask.ndim != 4 or mask.shape[2:] != (Lq, Lk) or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H):
+            raise ValueError("mask must be [1 or B, 1 or H, Lq, Lk]")
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    rp = 1.0 / (1.0 - float(np.float32(dropout_p)))
+    O = np.zeros((B, H, R, D), dtype=np.float64)
+    LSE = np.full((B, H, R), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kk = k[b, h].astype(np.float64)
+            vv = v[b, h].astype(np.float64)
+            for r0 in range(0, R, row_block):
+                rr = rows[r0:r0 + row_block]
+                a = scale * (q[b, h, rr].astype(np.float64) @ kk.T)
+                allowed = _allowed_keys(rr, Lq, Lk, causal)
+                if mask is not None:
+                    ok, add = _mask_block(mask, mask_kind, b, h, rr, Lk)
+                    allowed = allowed & ok
+                    a = a + add
+                a = np.where(allowed, a, -np.inf)
+                live = allowed.any(axis=1)
+                m = np.where(live, a.max(axis=1), 0.0)
+                e = np.where(allowed, np.exp(a - m[:, None]), 0.0)
+                s = e.sum(axis=1)
+                p = np.where(live[:, None], e / np.where(live, s, 1.0)[:, None], 0.0)
+                if dropout_p:
+                    p = p * keep_pattern(seed, offset, b * H + h, rr, Lk, dropout_p) * rp
+                O[b, h, r0:r0 + len(rr)] = p @ vv
+                LSE[b, h, r0:r0 + len(rr)] = np.where(live, m + np.log(np.where(live, s, 1.0)), -np.inf)
+    return O, LSE
+
+
+def attention_ex_bwd(q, k, v, do, scale: float, causal: bool = False, mask=None, mask_kind=None,
+                     dropout_p: float = 0.0, seed: int = 0, offset: int = 0, row_block: int = 1024):
+    """Gradients of ``attention_ex``'s O with respect to q, k and v, float64.
+
+    The chain rule of O = (P o Z / (1 - p)) V with P the masked softmax of
+    a = scale q k^T (+ additive mask): with dP~ = (Z / (1 - p)) o (dO V^T),
+      dV = (P o Z / (1 - p))^T dO,
+      dA_ij = P_ij (dP~_ij - sum_l P_il dP~_il),
+      dQ = scale dA K,  dK = scale dA^T Q.
+    No gradient is returned for the mask.  Returns (dQ, dK, dV).
+    """
+    from .philox import keep_pattern
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if mask is not None:
+        mask = np.asarray(mask)
+    rp = 1.0 / (1.0 - float(np.float32(dropout_p)))
+    dQ = np.zeros((B, H, Lq, D))
+    dK = np.zeros((B, H, Lk, D))
+    dV = np.zeros((B, H, Lk, D))
+    for b in range(B):
+        for h in range(H):
+            kk = k[b, h].astype(np.float64)
+            vv = v[b, h].astype(np.float64)
+            for r0 in range(0, Lq, row_block):
+                rr = np.arange(r0, min(r0 + row_block, Lq))
+                qq = q[b, h, rr].astype(np.float64)
+                g = do[b, h, rr].astype(np.float64)
+                a = scale * (qq @ kk.T)
+                allowed = _allowed_keys(rr, Lq, Lk, causal)
+                if mask is not None:
+                    ok, add = _mask_block(mask, mask_kind, b, h, rr, Lk)
+                    allowed = allowed & ok
+                    a = a + add
+                a = np.where(allowed, a, -np.inf)
+                live = allowed.any(axis=1)
+                m = np.where(live, a.max(axis=1), 0.0)
+                e = np.where(allowed, np.exp(a - m[:, None]), 0.0)
+                s = e.sum(axis=1)
+                p = np.where(live[:, None], e / np.where(live, s, 1.0)[:, None], 0.0)
+                z = keep_pattern(seed, offset, b * H + h, rr, Lk, dropout_p) * rp if dropout_p else 1.0
+                da = _softmax_vjp(p, z * (g @ vv.T))
+                dv, dk, dq = _score_grads(p * z, da, qq, kk, g, scale)
+                dV[b, h] += dv
+                dK[b, h] += dk
+                dQ[b, h, rr] = dq
     return dQ, dK, dV
 
 
