@@ -64,8 +64,17 @@ typedef enum {
   ATTN_ERR_SPLITS = -7,         /* num_splits outside [0, ATTN_MAX_SPLITS] */
   ATTN_ERR_ALIAS = -8,          /* o or lse overlaps an input or each other */
   ATTN_ERR_ALIGN = -9,          /* a tensor pointer is not 16-byte aligned */
-  ATTN_ERR_HIP = -10            /* a HIP launch or allocation failed */
+  ATTN_ERR_HIP = -10,           /* a HIP launch or allocation failed */
+  ATTN_ERR_MASK = -11,          /* bad mask_kind, or mask_b / mask_h not 1 or B / H */
+  ATTN_ERR_DROPOUT = -12        /* dropout_p outside [0, 1) */
 } attn_status_t;
+
+/* Kinds of the general mask of attn_fwd_ex / attn_bwd_ex. */
+typedef enum {
+  ATTN_MASK_NONE = 0,  /* no mask argument (causal still applies) */
+  ATTN_MASK_BOOL = 1,  /* uint8: nonzero = the query attends to the key */
+  ATTN_MASK_ADD = 2    /* float32 added to the scaled score; -inf excludes the key */
+} attn_mask_kind_t;
 
 /* Largest split count accepted by attn_decode_fwd and attn_decode_varlen_fwd. */
 #define ATTN_MAX_SPLITS 256
@@ -158,6 +167,51 @@ int attn_decode_varlen_fwd(const void* q, const void* k, const void* v, void* o,
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D,
              int causal, float scale, void* stream, int dtype);
+
+/*
+ * attn_fwd_ex - attention forward with a general mask and dropout fused into
+ * the tile.
+ *
+ * The comfyai.app chapter "6.3 FlashAttention" (section 6.3.3, "Kernel
+ * Fusion") runs scores, scale, mask, softmax, dropout and the value product
+ * of a tile in one kernel; this entry point does the same with:
+ *   - mask: [mask_b, mask_h, Lq, Lk] contiguous (mask_b in {1, B}, mask_h in
+ *     {1, H}; a size-1 axis is broadcast), a DEVICE pointer, 16-byte
+ *     aligned, of kind ATTN_MASK_BOOL (uint8) or ATTN_MASK_ADD (float32
+ *     added to scale * q.k); ignored (may be NULL) for ATTN_MASK_NONE.  It
+ *     combines with causal: a key is excluded if either excludes it.
+ *   - dropout_p in [0, 1): each weight P_ij is kept iff word (j mod 4) of
+ *     Philox4x32-10 (Salmon et al., SC 2011) with counter
+ *     (j / 4, i, b * H + h, offset) and key (seed low 32 bits, seed high 32
+ *     bits) is >= floor(dropout_p * 2^32); kept weights are scaled by
+ *     1 / (1 - dropout_p).  lse is computed from the weights before dropout.
+ *     The same (seed, offset) gives the same pattern in attn_bwd_ex.
+ * A row with no key left gets o = 0 and lse = -inf.  Shapes, lse and the
+ * other conventions as for attn_fwd; dtype ATTN_F16 or ATTN_BF16.  With
+ * ATTN_MASK_NONE and dropout_p == 0 this is attn_fwd.  o and lse must not
+ * overlap the mask.  Allocates nothing.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Lq, int Lk, int D, int causal, float scale,
+                const void* mask, int mask_kind, int mask_b, int mask_h,
+                float dropout_p, unsigned long long seed, unsigned int offset,
+                void* stream, int dtype);
+
+/*
+ * attn_bwd_ex - gradients of attn_fwd_ex's o with respect to q, k, v.
+ *
+ * Arguments as attn_bwd plus the mask and dropout arguments of the forward
+ * call (the same values: the keep pattern is regenerated from seed and
+ * offset).  With dropout the chain rule runs through the kept, rescaled
+ * weights: dv = (P o Z / (1 - p))^T dout and ds = P o ((Z / (1 - p)) o
+ * (dout v^T) - rowsum(dout o o)).  No gradient is returned for the mask.
+ * dq, dk, dv must not overlap the mask.  Workspace as for attn_bwd.
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
+                int D, int causal, float scale, const void* mask, int mask_kind, int mask_b,
+                int mask_h, float dropout_p, unsigned long long seed, unsigned int offset,
+                void* stream, int dtype);
 
 /*
  * attn_decode_auto_splits - the split count attn_fwd and attn_decode_fwd

@@ -22,8 +22,9 @@ LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
-EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_bwd", "attn_decode_auto_splits",
-            "attn_strerror")
+EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_bwd", "attn_fwd_ex", "attn_bwd_ex",
+            "attn_decode_auto_splits", "attn_strerror")
+ATTN_MASK_NONE, ATTN_MASK_BOOL, ATTN_MASK_ADD = 0, 1, 2
 
 _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
@@ -60,6 +61,12 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_varlen_fwd.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
         lib.attn_bwd.restype = i
+        u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i, i, f, u64, u32, vp, i]
+        lib.attn_fwd_ex.restype = i
+        lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i, i, i, f, u64, u32,
+                                    vp, i]
+        lib.attn_bwd_ex.restype = i
         lib.attn_decode_auto_splits.argtypes = [i, i, i, i]
         lib.attn_decode_auto_splits.restype = i
         lib.attn_strerror.argtypes = [i]
@@ -201,6 +208,75 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
                         int(bool(causal)), scale, _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return dq, dk, dv
+
+
+def _mask_args(mask, B, H, Lq, Lk):
+    """(pointer, kind, mask_b, mask_h) of an optional mask tensor: bool or
+    uint8 -> boolean mask, float32 -> additive mask; shape [1|B, 1|H, Lq, Lk]."""
+    if mask is None:
+        return None, ATTN_MASK_NONE, 1, 1
+    if not isinstance(mask, torch.Tensor) or not mask.is_cuda or not mask.is_contiguous() or mask.dim() != 4:
+        raise ValueError("mask must be a contiguous 4-d GPU tensor")
+    if mask.dtype in (torch.bool, torch.uint8):
+        kind = ATTN_MASK_BOOL
+    elif mask.dtype == torch.float32:
+        kind = ATTN_MASK_ADD
+    else:
+        raise ValueError("mask dtype must be bool, uint8 (keep / drop) or float32 (additive)")
+    mb, mh, mq, mk = mask.shape
+    if mq != Lq or mk != Lk:
+        raise ValueError("mask must be [1 or B, 1 or H, Lq, Lk]")
+    return mask.data_ptr(), kind, mb, mh
+
+
+def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                scale: Optional[float] = None, mask: Optional[torch.Tensor] = None, dropout_p: float = 0.0,
+                seed: int = 0, offset: int = 0, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention with a general mask and dropout through ``attn_fwd_ex``.
+
+    mask: None, a bool / uint8 tensor (nonzero = attend) or a float32 tensor
+    added to the scaled scores, shaped [1 or B, 1 or H, Lq, Lk].  dropout_p
+    in [0, 1) with the Philox key ``seed`` (64-bit) and counter word
+    ``offset`` (32-bit).  float16 / bfloat16 only.
+    """
+    lib = load()
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    out, lse = _prep(q, k, v, out, lse, Lq)
+    mp, kind, mb, mh = _mask_args(mask, B, H, Lq, Lk)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Lq, Lk,
+                           D, int(bool(causal)), scale, mp, kind, mb, mh, float(dropout_p), int(seed), int(offset),
+                           _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return out, lse
+
+
+def attn_bwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                dout: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+                mask: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0,
+                dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                dv: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dq, dk, dv of ``attn_fwd_ex`` (same mask and dropout arguments)."""
+    lib = load()
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    _prep(q, k, v, out, lse, Lq)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a GPU tensor shaped and typed like q")
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    mp, kind, mb, mh = _mask_args(mask, B, H, Lq, Lk)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
+                           int(bool(causal)), scale, mp, kind, mb, mh, float(dropout_p), int(seed), int(offset),
+                           _stream_handle(stream), _DTYPE_CODES[q.dtype]))
     return dq, dk, dv
 
 

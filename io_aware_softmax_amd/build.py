@@ -16,7 +16,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 SOURCES = ["api.hip", "device_info.hip", "prefill_mfma.hip", "prefill_pp.hip", "prefill_f32.hip", "decode.hip",
-           "backward.hip"]
+           "backward.hip", "prefill_ex.hip"]
 LIB = PKG / "libattn.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

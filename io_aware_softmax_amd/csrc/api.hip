@@ -113,6 +113,95 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   return ATTN_OK;
 }
 
+// Checks and packs the mask / dropout arguments shared by attn_fwd_ex and
+// attn_bwd_ex.  `outs` / `out_n`: the call's output buffers, which must not
+// overlap the mask.
+int make_mask_dropout(const void* mask, int mask_kind, int mask_b, int mask_h, float dropout_p,
+                      unsigned long long seed, unsigned offset, int B, int H, int Lq, int Lk,
+                      const void* const* outs, const size_t* out_n, int n_outs, attn::MaskDropout* md) {
+  if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_BOOL && mask_kind != ATTN_MASK_ADD)
+    return ATTN_ERR_MASK;
+  if (!(dropout_p >= 0.f && dropout_p < 1.f)) return ATTN_ERR_DROPOUT;  // also rejects NaN
+  md->mask = nullptr;
+  md->kind = mask_kind;
+  md->mask_b = md->mask_h = 1;
+  md->H = H;
+  if (mask_kind != ATTN_MASK_NONE) {
+    if (mask == nullptr) return ATTN_ERR_NULL;
+    if ((mask_b != 1 && mask_b != B) || (mask_h != 1 && mask_h != H)) return ATTN_ERR_MASK;
+    if (reinterpret_cast<uintptr_t>(mask) & 15u) return ATTN_ERR_ALIGN;
+    const size_t nm = size_t(mask_b) * mask_h * Lq * Lk * (mask_kind == ATTN_MASK_BOOL ? 1 : 4);
+    for (int i = 0; i < n_outs; ++i)
+      if (overlaps(outs[i], out_n[i], mask, nm)) return ATTN_ERR_ALIAS;
+    md->mask = mask;
+    md->mask_b = mask_b;
+    md->mask_h = mask_h;
+  }
+  md->dropout = dropout_p > 0.f;
+  const double thr = std::floor(double(dropout_p) * 4294967296.0);
+  md->thr = thr >= 4294967295.0 ? 0xFFFFFFFFu : unsigned(thr);
+  md->rp = float(1.0 / (1.0 - double(dropout_p)));
+  md->k0 = unsigned(seed & 0xFFFFFFFFull);
+  md->k1 = unsigned(seed >> 32);
+  md->offset = offset;
+  return ATTN_OK;
+}
+
+// The backward behind attn_bwd and attn_bwd_ex (md: mask / dropout or NULL).
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+            void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk, int D, int causal, float scale,
+            hipStream_t s, int dtype, const attn::MaskDropout* md) {
+  if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  // The forward's checks cover q, k, v, o, lse, the sizes, scale and causal.
+  int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if (mis & 15u) return ATTN_ERR_ALIGN;
+  const int64_t BH = int64_t(B) * H;
+  const size_t es = elem_bytes(dtype);
+  const size_t nq = size_t(BH) * Lq * D * es, nk = size_t(BH) * Lk * D * es;
+  const size_t nl = size_t(BH) * Lq * sizeof(float);
+  // Outputs must not overlap any input or each other.
+  const void* in[6] = {q, k, v, o, dout, lse};
+  const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
+  void* out[3] = {dq, dk, dv};
+  const size_t out_n[3] = {nq, nk, nk};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], out_n[i], in[j], in_n[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(out[i], out_n[i], out[j], out_n[j])) return ATTN_ERR_ALIAS;
+  }
+  if (BH * ((int64_t(Lk) + 127) / 128) > kMaxWorkgroups || BH * ((int64_t(Lq) + 63) / 64) > kMaxWorkgroups)
+    return ATTN_ERR_DIM;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_workspace_bytes(int(BH), Lq), s);
+  if (e != hipSuccess) return hip_fail(e);
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.stats = static_cast<float*>(ws);
+  a.BH = int(BH);
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.c = scale * attn::kLog2e;
+  a.scale = scale;
+  e = attn::launch_bwd(dtype, D, causal != 0, a, s, md);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return ATTN_OK;
+}
+
 }  // namespace
 
 ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -177,56 +266,61 @@ ATTN_EXPORT int attn_decode_varlen_fwd(const void* q, const void* k, const void*
 ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
                          int D, int causal, float scale, void* stream, int dtype) {
-  if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
-  // The forward's checks cover q, k, v, o, lse, the sizes, scale and causal.
-  int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, causal, scale,
+                 static_cast<hipStream_t>(stream), dtype, nullptr);
+}
+
+ATTN_EXPORT int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                            int H, int Lq, int Lk, int D, int causal, float scale, const void* mask,
+                            int mask_kind, int mask_b, int mask_h, float dropout_p,
+                            unsigned long long seed, unsigned offset, void* stream, int dtype) {
+  const int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
   if (st != ATTN_OK) return st;
   if (dtype == ATTN_F32) return ATTN_ERR_DTYPE;
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
-                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
-  if (mis & 15u) return ATTN_ERR_ALIGN;
-  const int64_t BH = int64_t(B) * H;
   const size_t es = elem_bytes(dtype);
-  const size_t nq = size_t(BH) * Lq * D * es, nk = size_t(BH) * Lk * D * es;
-  const size_t nl = size_t(BH) * Lq * sizeof(float);
-  // Outputs must not overlap any input or each other.
-  const void* in[6] = {q, k, v, o, dout, lse};
-  const size_t in_n[6] = {nq, nk, nk, nq, nq, nl};
-  void* out[3] = {dq, dk, dv};
-  const size_t out_n[3] = {nq, nk, nk};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(out[i], out_n[i], in[j], in_n[j])) return ATTN_ERR_ALIAS;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlaps(out[i], out_n[i], out[j], out_n[j])) return ATTN_ERR_ALIAS;
-  }
-  if (BH * ((int64_t(Lk) + 127) / 128) > kMaxWorkgroups || BH * ((int64_t(Lq) + 63) / 64) > kMaxWorkgroups)
-    return ATTN_ERR_DIM;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::bwd_workspace_bytes(int(BH), Lq), s);
-  if (e != hipSuccess) return hip_fail(e);
-  attn::BwdArgs a;
+  const void* outs[2] = {o, lse};
+  const size_t out_n[2] = {size_t(B) * H * Lq * D * es, size_t(B) * H * Lq * sizeof(float)};
+  attn::MaskDropout md;
+  const int sm = make_mask_dropout(mask, mask_kind, mask_b, mask_h, dropout_p, seed, offset, B, H, Lq, Lk,
+                                   outs, out_n, 2, &md);
+  if (sm != ATTN_OK) return sm;
+  if (mask_kind == ATTN_MASK_NONE && !md.dropout)
+    return attn_fwd(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, stream, dtype);
+  if (int64_t(B) * H * ((int64_t(Lq) + 127) / 128) > kMaxWorkgroups) return ATTN_ERR_DIM;
+  attn::PrefillArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
-  a.dout = dout;
   a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.stats = static_cast<float*>(ws);
-  a.BH = int(BH);
+  a.BH = B * H;
   a.Lq = Lq;
   a.Lk = Lk;
-  a.c = scale * attn::kLog2e;
-  a.scale = scale;
-  e = attn::launch_bwd(dtype, D, causal != 0, a, s);
-  const hipError_t ef = hipFreeAsync(ws, s);
-  if (e != hipSuccess) return hip_fail(e);
-  if (ef != hipSuccess) return hip_fail(ef);
-  return ATTN_OK;
+  a.c = std::fabs(scale) * attn::kLog2e;
+  a.neg = scale < 0.f;
+  const hipError_t e = attn::launch_prefill_ex(dtype, D, causal != 0, a, md, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+ATTN_EXPORT int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
+                            int D, int causal, float scale, const void* mask, int mask_kind, int mask_b,
+                            int mask_h, float dropout_p, unsigned long long seed, unsigned offset,
+                            void* stream, int dtype) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  // Sizes first (the mask's extent below needs them valid).
+  int st = validate(q, k, v, o, lse, B, H, Lq, Lk, D, causal, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t es = elem_bytes(dtype);
+  const void* outs[3] = {dq, dk, dv};
+  const size_t out_n[3] = {size_t(B) * H * Lq * D * es, size_t(B) * H * Lk * D * es,
+                           size_t(B) * H * Lk * D * es};
+  attn::MaskDropout md;
+  st = make_mask_dropout(mask, mask_kind, mask_b, mask_h, dropout_p, seed, offset, B, H, Lq, Lk, outs, out_n, 3,
+                         &md);
+  if (st != ATTN_OK) return st;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Lq, Lk, D, causal, scale,
+                 static_cast<hipStream_t>(stream), dtype, &md);
 }
 
 ATTN_EXPORT int attn_decode_auto_splits(int B, int H, int Lk, int D) {
@@ -248,6 +342,8 @@ ATTN_EXPORT const char* attn_strerror(int status) {
     case ATTN_ERR_SPLITS: return "num_splits must be in [0, ATTN_MAX_SPLITS]";
     case ATTN_ERR_ALIAS: return "o or lse overlaps an input or each other";
     case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_MASK: return "mask_kind is not an attn_mask_kind_t, or mask_b / mask_h is not 1 or B / H";
+    case ATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1)";
     case ATTN_ERR_HIP:
       std::snprintf(g_status_msg, sizeof(g_status_msg), "HIP error: %s", g_hip_msg);
       return g_status_msg;

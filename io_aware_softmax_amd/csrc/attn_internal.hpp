@@ -60,6 +60,20 @@ struct BwdArgs {
   float scale;
 };
 
+// General mask and dropout of the fused tile (forward and backward).
+struct MaskDropout {
+  const void* mask;  // [mask_b, mask_h, Lq, Lk] uint8 (kind 1) or float32 (kind 2); nullptr for kind 0
+  int kind;          // 0 none, 1 boolean (nonzero = attend), 2 additive (float32, -inf = excluded)
+  int mask_b;        // 1 (broadcast over batch) or B
+  int mask_h;        // 1 (broadcast over heads) or H
+  int H;             // heads: bh = b * H + h
+  bool dropout;      // p > 0
+  unsigned thr;      // keep iff the Philox word is >= thr = floor(p 2^32)
+  float rp;          // 1 / (1 - p)
+  unsigned k0, k1;   // Philox key: the seed's low and high words
+  unsigned offset;   // Philox counter word 3
+};
+
 // Workgroups of `kernel` (block threads, static LDS only) that device `dev`
 // holds resident at once: compute units times workgroups per unit.  Cached.
 hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out);
@@ -70,8 +84,13 @@ hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs&
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
 // The same algorithm with fp32 inputs on the fp32 MFMA.
 hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
-// Attention backward (16-bit dtypes): stats, dK/dV and dQ kernels on stream s.
-hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s);
+// Forward with a general mask and / or dropout (16-bit dtypes).
+hipError_t launch_prefill_ex(int dtype, int D, bool causal, const PrefillArgs& a, const MaskDropout& md,
+                             hipStream_t s);
+// Attention backward (16-bit dtypes): stats, dK/dV and dQ kernels on stream s;
+// md == nullptr: no mask and no dropout.
+hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s,
+                      const MaskDropout* md = nullptr);
 // Bytes of BwdArgs::stats for B * H = BH and Lq queries.
 size_t bwd_workspace_bytes(int BH, int Lq);
 // Split-KV decode: partials then combine, both on stream s.

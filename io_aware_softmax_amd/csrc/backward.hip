@@ -38,57 +38,19 @@
 #include <utility>
 
 #include "attn_internal.hpp"
+#include "mask_dropout.hpp"
 #include "mfma_tile.hpp"
+#include "swz_tile.hpp"
 
 namespace attn {
 namespace {
 
 using namespace mt;
+using namespace st;
 
 constexpr int NT = 256;   // threads per workgroup (4 waves)
-constexpr int BQ = 64;    // rows per LDS tile (queries for dK/dV, keys for dQ)
 constexpr int BW = 128;   // rows owned by a workgroup (4 waves x 32)
 constexpr int kStatFloats = 2 * BQ;  // per stats tile: lse2[64], then Dv[64]
-
-template <int D>
-struct SwzTile {
-  static constexpr int CPR = D / 8;       // 16-byte chunks per row
-  static constexpr int PITCH = D * 2;     // bytes per row (no padding)
-  static constexpr int BYTES = BQ * PITCH;
-  static constexpr int INST = BYTES / 1024;  // 64-lane DMA instructions per tile
-  static constexpr int PER_WAVE = INST / 4;
-  static_assert(INST % 4 == 0, "tile DMA splits evenly over 4 waves");
-  // Chunk permutation of row r (depends on r mod 16 only).
-  //  D = 128 (one row spans all 64 banks): bits 0-1 of r go to bits 2-3 of
-  //   the chunk, bits 2-3 of r to bits 0-1.  16 consecutive rows: 16
-  //   distinct chunks.  4 consecutive rows (r mod 4 = 0..3): 4 distinct
-  //   4-chunk groups.
-  //  D = 64 (two rows per 64 banks, bit 0 of r picks the half): bit 1 of r
-  //   goes to bit 2 of the chunk, bits 2-3 of r to bits 0-1.
-  __device__ static int swz(int r) {
-    if constexpr (D == 128)
-      return ((r & 3) << 2) | ((r >> 2) & 3);
-    else
-      return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-};
-
-// DMA of one 64-row tile (row 0 at `src`) into swizzled LDS.  Rows at or
-// past rows_left (>= 1) fetch row rows_left - 1 instead (in bounds; their
-// results are discarded or zero-weighted).  `src` must be wave-uniform.
-template <int D>
-__device__ __forceinline__ void dma_swz_tile(const char* src, char* dst, int w, int lane, int rows_left) {
-  using T = SwzTile<D>;
-#pragma unroll
-  for (int i = 0; i < T::PER_WAVE; ++i) {
-    const int inst = w * T::PER_WAVE + i;
-    const int slot = inst * 64 + lane;
-    const int row = slot / T::CPR, pc = slot % T::CPR;
-    const int r = row < rows_left ? row : rows_left - 1;
-    const unsigned off = (unsigned)r * (D * 2) + 16u * (unsigned)(pc ^ T::swz(row));
-    dma_run<1>(src, &off, lds_addr(dst + inst * 1024));
-  }
-}
 
 // One stats tile (512 B) into LDS; lanes 32-63 fetch the same bytes again
 // into the following 512 B (a whole instruction, never read).
@@ -96,8 +58,6 @@ __device__ __forceinline__ void dma_stats(const float* src, char* dst, int lane)
   const unsigned off = 16u * (unsigned)(lane & 31);
   dma_run<1>(reinterpret_cast<const char*>(src), &off, lds_addr(dst));
 }
-
-__device__ __forceinline__ void land_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool BF16>
 __device__ __forceinline__ float load16(const unsigned short* p) {
@@ -108,10 +68,6 @@ __device__ __forceinline__ float load16(const unsigned short* p) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// Bit-permuted row read by lane n for products over D: bits 2 and 3 of n
-// swapped, so that accumulator register r of the 32 x 32 result holds row
-// 16 (r / 8) + 8 h + r % 8 -- the rows of the next product's k-steps.
-__device__ __forceinline__ int perm_row(int n) { return (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1); }
 
 // ---------------------------------------------------------------------------
 // stats: lse2 = lse * log2(e) and Dv = rowsum(dO o O), tile-blocked.
@@ -182,15 +138,6 @@ struct BwdSlots {
   static_assert(E1 + 3 < 2 * NS + NG && E1 + 7 < 2 * NS + NG + NG / 2, "block 1 elements late");
 };
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled.
-template <int N, class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
 
 template <bool BF16, int D, class Hook>
 __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, const float* st,
@@ -262,8 +209,10 @@ __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, 
     __builtin_amdgcn_sched_barrier(0);
   });
 }
-template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
+// EX: a general mask and / or dropout (md) apply; the slot-scheduled fast
+// path is then off and every tile goes block by block.
+template <bool BF16, int D, bool CAUSAL, bool EX>
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout md) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;  // k-steps of a product over D
   constexpr int DB = D / 32;  // 32-column blocks of D
@@ -336,6 +285,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
       ta[db][hi] = row * T::PITCH + 16 * (chunk ^ T::swz(row)) + 8 * (li & 1);
     }
 
+  const size_t mslab = EX && md.kind != 0 ? mask_slab(md, bh, Lq, Lk) : 0;
+  const PhiloxKey pk{md.k0, md.k1};
+
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -372,13 +324,25 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
     s16x8 pa[2], sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-      if (masked) {
-        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-        if (key > qi + off) p = 0.f;
+      const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+      float mt = 0.f;  // mask term (base 2)
+      if constexpr (EX) {
+        if (md.kind != 0 && qi < Lq && key < Lk) mt = mask_term(md, mslab + (size_t)qi * Lk + key);
       }
-      const float ds = p * (dp[r] - dd[r]);
-      pa[r >> 3][r & 7] = (short)round16<BF16>(p);
+      float p = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt - l2[r]));
+      if (masked && key > qi + off) p = 0.f;
+      // Dropout: the value product sees the kept weights scaled by 1/(1-p),
+      // and dP reaches the softmax through the same factors.
+      float pv = p, dpk = dp[r];
+      if constexpr (EX) {
+        if (md.dropout) {
+          const bool kp = dropout_keep1(pk, key, qi, bh, md.offset, md.thr);
+          pv = kp ? p * md.rp : 0.f;
+          dpk = kp ? dpk * md.rp : 0.f;
+        }
+      }
+      const float ds = p * (dpk - dd[r]);
+      pa[r >> 3][r & 7] = (short)round16<BF16>(pv);
       sa[r >> 3][r & 7] = (short)round16<BF16>(ds);
     }
     // dV += P^T dO and dK += dS^T Q over the block's 32 queries (2 k-steps).
@@ -416,7 +380,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // block by block.
   auto tile = [&](char* stage, int q0, char* nstage, int tn) __attribute__((always_inline)) {
     const bool has_next = tn < nqt;
-    if (q0 + BQ <= Lq && (!CAUSAL || q0 + off >= kw0 + 31)) {
+    if (!EX && q0 + BQ <= Lq && (!CAUSAL || q0 + off >= kw0 + 31)) {
       const int tf = has_next ? tn : tn - 1;
       const int rows_left = min(BQ, Lq - tf * BQ);
       unsigned cur[T::PER_WAVE];
@@ -489,8 +453,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 128 queries, loop over 64-key tiles.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
+template <bool BF16, int D, bool CAUSAL, bool EX>
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -551,6 +515,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     l2 = st[qi % BQ];
     dd = st[BQ + qi % BQ];
   }
+  // Row of the lane's query in the mask (row 0 of the slab for padded
+  // queries: in bounds, never stored).
+  const size_t mrow = EX && md.kind != 0 ? mask_slab(md, bh, Lq, Lk) + (size_t)(qi < Lq ? qi : 0) * Lk : 0;
+  const PhiloxKey pk{md.k0, md.k1};
 
   const int prow = perm_row(n);
   unsigned ra[KS];
@@ -585,15 +553,31 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     // Register r holds key kb0 + 16 (r / 8) + 8 h + r % 8 of query qi.
     const bool masked = kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off);
+    float mt[16];
+    unsigned keep[2] = {0xffu, 0xffu};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt[r] = 0.f;
+    if constexpr (EX) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key0 = kb0 + 16 * half + 8 * h;
+        if (md.kind != 0) mask_terms8(md, mrow + key0, key0, Lk, *reinterpret_cast<float(*)[8]>(mt + 8 * half));
+        if (md.dropout) keep[half] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
+      }
+    }
     s16x8 sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+      float p = mt[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt[r] - l2));
       if (masked) {
         const int kj = kb0 + 16 * (r >> 3) + 8 * h + (r & 7);
         if (kj >= Lk || (CAUSAL && kj > qi + off)) p = 0.f;
       }
-      sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dp[r] - dd));
+      float dpk = dp[r];
+      if constexpr (EX) {
+        if (md.dropout) dpk = ((keep[r >> 3] >> (r & 7)) & 1u) ? dpk * md.rp : 0.f;
+      }
+      sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dpk - dd));
     }
     // dQ += dS K over the block's 32 keys (2 k-steps).
 #pragma unroll
@@ -638,18 +622,18 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int DT, int D, bool CAUSAL>
-hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
+template <int DT, int D, bool CAUSAL, bool EX>
+hipError_t launch_typed(const BwdArgs& a, const MaskDropout& md, hipStream_t s) {
   const int nqt = (a.Lq + BQ - 1) / BQ;
   bwd_stats_kernel<DT, D><<<dim3(a.BH * nqt), dim3(NT), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (a.Lk + BW - 1) / BW;
   const int nqb = (a.Lq + BW - 1) / BW;
-  bwd_dkdv_kernel<DT == 2, D, CAUSAL><<<dim3(a.BH * nkb), dim3(NT), 0, s>>>(a);
+  bwd_dkdv_kernel<DT == 2, D, CAUSAL, EX><<<dim3(a.BH * nkb), dim3(NT), 0, s>>>(a, md);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dq_kernel<DT == 2, D, CAUSAL><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a);
+  bwd_dq_kernel<DT == 2, D, CAUSAL, EX><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md);
   return hipGetLastError();
 }
 
@@ -659,13 +643,19 @@ size_t bwd_workspace_bytes(int BH, int Lq) {
   return (size_t)BH * ((Lq + BQ - 1) / BQ) * kStatFloats * sizeof(float);
 }
 
-hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s) {
-  if (dtype == 2) {
-    if (D == 128) return causal ? launch_typed<2, 128, true>(a, s) : launch_typed<2, 128, false>(a, s);
-    return causal ? launch_typed<2, 64, true>(a, s) : launch_typed<2, 64, false>(a, s);
-  }
-  if (D == 128) return causal ? launch_typed<1, 128, true>(a, s) : launch_typed<1, 128, false>(a, s);
-  return causal ? launch_typed<1, 64, true>(a, s) : launch_typed<1, 64, false>(a, s);
+template <int DT, bool EX>
+hipError_t launch_ex(int D, bool causal, const BwdArgs& a, const MaskDropout& md, hipStream_t s) {
+  if (D == 128)
+    return causal ? launch_typed<DT, 128, true, EX>(a, md, s) : launch_typed<DT, 128, false, EX>(a, md, s);
+  return causal ? launch_typed<DT, 64, true, EX>(a, md, s) : launch_typed<DT, 64, false, EX>(a, md, s);
+}
+
+hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s, const MaskDropout* md) {
+  const bool ex = md != nullptr && (md->kind != 0 || md->dropout);
+  MaskDropout none{};
+  const MaskDropout& m = ex ? *md : none;
+  if (dtype == 2) return ex ? launch_ex<2, true>(D, causal, a, m, s) : launch_ex<2, false>(D, causal, a, m, s);
+  return ex ? launch_ex<1, true>(D, causal, a, m, s) : launch_ex<1, false>(D, causal, a, m, s);
 }
 
 }  // namespace attn

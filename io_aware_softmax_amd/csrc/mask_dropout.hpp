@@ -1,0 +1,59 @@
+// Reading a general attention mask and drawing dropout keep bits inside the
+// fused tile (the comfyai.app chapter "6.3 FlashAttention", section 6.3.3,
+// "Kernel Fusion": scores, scale, mask, softmax, dropout and the value
+// product in one kernel).  The mask kind is a run-time value (one kernel
+// serves boolean and additive masks); the branches on it are uniform.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_internal.hpp"
+#include "philox.hpp"
+
+namespace attn {
+
+// Element offset of the (b, h) slab of a [mask_b, mask_h, Lq, Lk] mask
+// (axes of size 1 broadcast).
+__device__ __forceinline__ size_t mask_slab(const MaskDropout& md, int bh, int Lq, int Lk) {
+  const int b = bh / md.H, h = bh % md.H;
+  const int slab = (md.mask_b == 1 ? 0 : b) * md.mask_h + (md.mask_h == 1 ? 0 : h);
+  return (size_t)slab * Lq * Lk;
+}
+
+// Base-2 additive term of one element (idx = slab + i Lk + j): 0 / -inf for
+// a boolean mask, bias * log2(e) for an additive one, 0 without a mask.
+__device__ __forceinline__ float mask_term(const MaskDropout& md, size_t idx) {
+  if (md.kind == 1) return static_cast<const unsigned char*>(md.mask)[idx] ? 0.f : -INFINITY;
+  if (md.kind == 2) return static_cast<const float*>(md.mask)[idx] * kLog2e;
+  return 0.f;
+}
+
+// Terms of keys j0 .. j0 + 7 of one query row (idx = slab + i Lk + j0);
+// keys at or past Lk get -inf.  One 8-byte (boolean) or two 16-byte
+// (additive) loads when the 8 keys are inside the row and aligned.
+__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, float (&t)[8]) {
+  if (md.kind == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? 0.f : -INFINITY;
+    return;
+  }
+  if (j0 + 8 <= Lk && idx % 8 == 0) {
+    if (md.kind == 1) {
+      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + idx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = (((e < 4 ? u.x : u.y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx + 4);
+      t[0] = a.x * kLog2e; t[1] = a.y * kLog2e; t[2] = a.z * kLog2e; t[3] = a.w * kLog2e;
+      t[4] = b.x * kLog2e; t[5] = b.y * kLog2e; t[6] = b.z * kLog2e; t[7] = b.w * kLog2e;
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? mask_term(md, idx + e) : -INFINITY;
+}
+
+}  // namespace attn

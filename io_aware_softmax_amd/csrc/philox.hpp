@@ -1,0 +1,58 @@
+// Philox4x32-10 counter-based generator on the device (Salmon, Moraes, Dror,
+// Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011, section 3.2
+// and table 2) and the dropout keep rule built on it.
+//
+// One round multiplies counter words 0 and 2 by M0 and M1 (full 64-bit
+// products), then outputs (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1,
+// lo(M0 x0)); the key is bumped by the Weyl constants between rounds.
+//
+// Dropout: the weight of (batch-head bh, query i, key j) is kept iff word
+// (j mod 4) of Philox4x32-10(counter = (j / 4, i, bh, offset),
+// key = (seed low, seed high)) is >= the threshold floor(p 2^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace attn {
+
+struct PhiloxKey {
+  unsigned k0, k1;
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 x, PhiloxKey key) {
+  constexpr unsigned M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr unsigned W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  unsigned k0 = key.k0, k1 = key.k1;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const unsigned hi0 = __umulhi(M0, x.x), lo0 = M0 * x.x;
+    const unsigned hi1 = __umulhi(M1, x.z), lo1 = M1 * x.z;
+    x = make_uint4(hi1 ^ x.y ^ k0, lo1, hi0 ^ x.w ^ k1, lo0);
+  }
+  return x;
+}
+
+// Keep bits of keys j0 .. j0 + 7 (j0 a multiple of 8) for query i: bit e is
+// key j0 + e.
+__device__ __forceinline__ unsigned dropout_keep8(PhiloxKey key, unsigned j0, unsigned i, unsigned bh,
+                                                  unsigned offset, unsigned thr) {
+  const uint4 a = philox4x32_10(make_uint4(j0 >> 2, i, bh, offset), key);
+  const uint4 b = philox4x32_10(make_uint4((j0 >> 2) + 1, i, bh, offset), key);
+  return (a.x >= thr ? 1u : 0u) | (a.y >= thr ? 2u : 0u) | (a.z >= thr ? 4u : 0u) | (a.w >= thr ? 8u : 0u) |
+         (b.x >= thr ? 16u : 0u) | (b.y >= thr ? 32u : 0u) | (b.z >= thr ? 64u : 0u) | (b.w >= thr ? 128u : 0u);
+}
+
+// Keep bit of one (query i, key j).
+__device__ __forceinline__ bool dropout_keep1(PhiloxKey key, unsigned j, unsigned i, unsigned bh, unsigned offset,
+                                              unsigned thr) {
+  const uint4 a = philox4x32_10(make_uint4(j >> 2, i, bh, offset), key);
+  const unsigned w = (j & 2) ? ((j & 1) ? a.w : a.z) : ((j & 1) ? a.y : a.x);
+  return w >= thr;
+}
+
+}  // namespace attn

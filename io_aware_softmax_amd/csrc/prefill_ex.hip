@@ -1,0 +1,232 @@
+// Attention forward with a general mask and dropout fused into the tile, for
+// fp16 / bf16 on gfx950 MFMA.
+//
+// The comfyai.app chapter "6.3 FlashAttention" (section 6.3.3, "Kernel
+// Fusion") lists the steps of one tile as scores, scale, mask, softmax,
+// dropout and the value product, all on chip.  Here a key of a row is
+// excluded when a boolean mask is zero, an additive mask is -inf, it lies
+// past Lk, or (causal) past the bottom-right diagonal; an additive mask is
+// added to the scaled scores.  The softmax statistics are the online ones of
+// the quidproquo.cc guide ("Mechanism: run with the wrong answer, then
+// correct it": running maximum d, denominator s, output corrected by
+// exp(d_old - d_new)) over the un-dropped weights, so LSE does not depend on
+// dropout; the weights that enter the value product are the kept ones, and
+// O is scaled by 1 / (1 - p) at the end.  A row with no key left gets O = 0
+// and LSE = -inf.
+//
+// Work decomposition: one workgroup = 4 waves x 32 queries; lane (n, h) of a
+// wave owns query n.  64-key tiles of K and V go HBM -> LDS by DMA (double
+// buffered, XOR-swizzled rows).  S^T = K Q^T puts 16 keys of the lane's
+// query in its registers, which are then directly the B operand (P^T) of
+// O^T += V^T P^T, V^T being read from LDS with ds_read_b64_tr_b16.  The mask
+// rows are read from device memory 8 keys at a time; the keep bits come from
+// two Philox4x32-10 blocks per 8 keys.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdint>
+
+#include "attn_internal.hpp"
+#include "mask_dropout.hpp"
+#include "mfma_tile.hpp"
+#include "swz_tile.hpp"
+
+namespace attn {
+namespace {
+
+using namespace mt;
+using namespace st;
+
+constexpr int NT = 256;
+constexpr int BW = 128;  // queries per workgroup
+
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDropout md, float c) {
+  using T = SwzTile<D>;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int STAGE = 2 * T::BYTES;  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int li = lane & 15, g = lane >> 4;
+  const int Lq = a.Lq, Lk = a.Lk;
+  const int off = Lk - Lq;
+  const int nqb = (Lq + BW - 1) / BW;
+  // Consecutive query blocks of one head share an XCD (same K / V);
+  // causal: the last query blocks (the most keys) go first.
+  const int total = a.BH * nqb;
+  const int wg = blockIdx.x;
+  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+  const int bh = logical / nqb;
+  const int qblk = CAUSAL ? nqb - 1 - logical % nqb : logical % nqb;
+  const int q0 = qblk * BW, wq0 = q0 + 32 * w;
+  const int q_last = min(q0 + BW, Lq) - 1;
+  const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
+  const int nkt = (kv_end + BQ - 1) / BQ;
+  const int w_key_end = wq0 >= Lq ? 0 : (CAUSAL ? min(Lk, min(wq0 + 31, Lq - 1) + off + 1) : Lk);
+
+  const char* Kb = static_cast<const char*>(a.k) + (size_t)bh * Lk * D * 2;
+  const char* Vb = static_cast<const char*>(a.v) + (size_t)bh * Lk * D * 2;
+  auto issue = [&](int j, char* stage) {
+    const int kv0 = j * BQ;
+    const int rows_left = min(BQ, Lk - kv0);
+    dma_swz_tile<D>(Kb + (size_t)kv0 * D * 2, stage, w, lane, rows_left);
+    dma_swz_tile<D>(Vb + (size_t)kv0 * D * 2, stage + T::BYTES, w, lane, rows_left);
+  };
+  issue(0, smem);
+
+  // Q of the lane's query as the B operand: Q[qi][16 t + 8 h .. + 8].
+  const int qi = wq0 + n;
+  const unsigned short* Qg = static_cast<const unsigned short*>(a.q) + (size_t)bh * Lq * D;
+  s16x8 qreg[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)qi * D + 16 * t + 8 * h);
+    qreg[t] = __builtin_bit_cast(s16x8, x);
+  }
+  const size_t mrow = md.kind != 0 && qi < Lq ? mask_slab(md, bh, Lq, Lk) + (size_t)qi * Lk : 0;
+  const PhiloxKey pk{md.k0, md.k1};
+
+  const int prow = perm_row(n);
+  unsigned ra[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) ra[t] = prow * T::PITCH + 16 * ((2 * t + h) ^ T::swz(prow));
+  unsigned ta[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * h + (li >> 2) + 4 * hi;
+      const int chunk = 4 * db + 2 * (g & 1) + ((li & 3) >> 1);
+      ta[db][hi] = row * T::PITCH + 16 * (chunk ^ T::swz(row)) + 8 * (li & 1);
+    }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;  // running maximum (base-2 units), same in both halves
+  float l_run = 0.f;        // this half's share of the denominator
+
+  auto tile = [&](const char* stage, int kv0) __attribute__((always_inline)) {
+    if (kv0 >= w_key_end) return;
+    const char* Ks = stage;
+    const char* Vs = stage + T::BYTES;
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+        s[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s[b]);
+    }
+    // Register r of block b holds key kv0 + 32 b + 16 (r / 8) + 8 h + r % 8.
+    float mx = -INFINITY;
+    unsigned keep[4] = {0xffu, 0xffu, 0xffu, 0xffu};
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int b = grp >> 1, half = grp & 1;
+      const int key0 = kv0 + 32 * b + 16 * half + 8 * h;
+      float t8[8];
+      mask_terms8(md, mrow + key0, key0, Lk, t8);
+      if (md.dropout) keep[grp] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * half + e;
+        float x = __builtin_fmaf(s[b][r], c, t8[e]);
+        if (CAUSAL && key0 + e > qi + off) x = -INFINITY;
+        s[b][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = halves_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+    s16x8 pb[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int b = grp >> 1, half = grp & 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(s[b][8 * half + e] - m_use);
+        psum += p;
+        pb[grp][e] = (short)round16<BF16>(((keep[grp] >> e) & 1u) ? p : 0.f);
+      }
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    // O^T += V^T P^T over the tile's four 16-key k-steps.
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* src = Vs + 16 * stp * T::PITCH;
+        const s16x4 lo = lds_read_tr(src + ta[db][0]);
+        const s16x4 hi = lds_read_tr(src + ta[db][1]);
+        oacc[db] = mfma32<BF16>(s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, pb[stp], oacc[db]);
+      }
+    }
+  };
+
+  land_all();
+  __syncthreads();
+  for (int j = 0; j < nkt; j += 2) {
+    if (j + 1 < nkt) issue(j + 1, smem + STAGE);
+    tile(smem, j * BQ);
+    land_all();
+    __syncthreads();
+    if (j + 1 >= nkt) break;
+    if (j + 2 < nkt) issue(j + 2, smem);
+    tile(smem + STAGE, (j + 1) * BQ);
+    land_all();
+    __syncthreads();
+  }
+
+  // Register r of block db holds column 32 db + 8 (r / 4) + 4 h + r % 4 of
+  // the lane's query.
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? (md.dropout ? md.rp : 1.f) / l_tot : 0.f;
+  if (qi < Lq) {
+    unsigned short* Og = static_cast<unsigned short*>(a.o) + ((size_t)bh * Lq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
+        const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(Og + 32 * db + 8 * jj + 4 * h) = make_uint2(lo, hi);
+      }
+    if (h == 0) a.lse[(size_t)bh * Lq + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch(const PrefillArgs& a, const MaskDropout& md, hipStream_t s) {
+  const int nqb = (a.Lq + BW - 1) / BW;
+  const float c = a.neg ? -a.c : a.c;
+  prefill_ex_kernel<BF16, D, CAUSAL><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md, c);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t dispatch_d(int D, bool causal, const PrefillArgs& a, const MaskDropout& md, hipStream_t s) {
+  if (D == 64) return causal ? launch<BF16, 64, true>(a, md, s) : launch<BF16, 64, false>(a, md, s);
+  return causal ? launch<BF16, 128, true>(a, md, s) : launch<BF16, 128, false>(a, md, s);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_ex(int dtype, int D, bool causal, const PrefillArgs& a, const MaskDropout& md,
+                             hipStream_t s) {
+  return dtype == 2 ? dispatch_d<true>(D, causal, a, md, s) : dispatch_d<false>(D, causal, a, md, s);
+}
+
+}  // namespace attn

@@ -183,3 +183,23 @@ def ragged_lengths(seed: int, B: int, Lk_max: int, lo: int = 1) -> np.ndarray:
     uniformly from [lo, Lk_max] by ``SeedSequence([seed, 3])``."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
     return rng.integers(lo, Lk_max + 1, size=B, dtype=np.int64).astype(np.int32)
+
+
+def bool_mask(seed: int, shape: Sequence[int], keep: float = 0.6, empty_rows: int = 0) -> np.ndarray:
+    """uint8 mask of ``shape`` ([Bm, Hm, Lq, Lk]): each entry 1 with
+    probability ``keep`` (``SeedSequence([seed, 6])``); the first
+    ``empty_rows`` query rows of slab (0, 0) are all zero."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 6])))
+    m = (rng.random(tuple(shape)) < keep).astype(np.uint8)
+    m[0, 0, :empty_rows] = 0
+    return m
+
+
+def additive_mask(seed: int, shape: Sequence[int], sigma: float = 2.0, neg_inf: float = 0.1) -> np.ndarray:
+    """float32 mask of ``shape``: N(0, sigma^2) entries, a fraction
+    ``neg_inf`` of them -inf (``SeedSequence([seed, 7])``)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    m = (rng.standard_normal(tuple(shape)) * sigma).astype(np.float32)
+    m[rng.random(tuple(shape)) < neg_inf] = -np.inf
+    return m
+

@@ -134,11 +134,37 @@ def test_backward_validation_errors(lib):
         assert _bwd(lib, **{kw: {"do": 5 * G, "dq": 7 * G, "dk": 8 * G, "dv": 9 * G}[kw] + 8}) == e["ATTN_ERR_ALIGN"]
 
 
+def test_ex_validation_errors(lib):
+    e = {n: _header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_DTYPE", "ATTN_ERR_MASK", "ATTN_ERR_DROPOUT",
+                                       "ATTN_ERR_ALIAS", "ATTN_ERR_ALIGN", "ATTN_ERR_DIM")}
+
+    def fwd(mask=10 * G, kind=1, mb=1, mh=3, p=0.0, dtype=2, o=4 * G, Lq=16):
+        return lib.attn_fwd_ex(G, 2 * G, 3 * G, o, 5 * G, 2, 3, Lq, 16, 64, 0, 0.125, mask, kind, mb, mh, p, 7, 0,
+                               None, dtype)
+
+    def bwd(mask=10 * G, kind=2, mb=2, mh=1, p=0.0, dq=7 * G):
+        return lib.attn_bwd_ex(G, 2 * G, 3 * G, 4 * G, 5 * G, 6 * G, dq, 8 * G, 9 * G, 2, 3, 16, 16, 64, 0, 0.125,
+                               mask, kind, mb, mh, p, 7, 0, None, 2)
+    assert fwd(mask=0) == e["ATTN_ERR_NULL"]
+    assert fwd(kind=3) == e["ATTN_ERR_MASK"] and fwd(kind=-1) == e["ATTN_ERR_MASK"]
+    assert fwd(mb=3) == e["ATTN_ERR_MASK"] and fwd(mh=2) == e["ATTN_ERR_MASK"]
+    assert fwd(mask=10 * G + 8) == e["ATTN_ERR_ALIGN"]
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert fwd(p=p) == e["ATTN_ERR_DROPOUT"]
+    assert fwd(dtype=0) == e["ATTN_ERR_DTYPE"]
+    assert fwd(o=10 * G + 256) == e["ATTN_ERR_ALIAS"]        # o inside the mask
+    assert fwd(Lq=0) == e["ATTN_ERR_DIM"]
+    assert bwd(dq=10 * G + 64) == e["ATTN_ERR_ALIAS"]        # dq inside the additive mask
+    assert bwd(kind=5) == e["ATTN_ERR_MASK"]
+    assert bwd(p=2.0) == e["ATTN_ERR_DROPOUT"]
+    assert bwd(mask=0) == e["ATTN_ERR_NULL"]
+
+
 def test_strerror_and_auto_splits(lib):
-    for code in range(-10, 1):
+    for code in range(-12, 1):
         msg = binding.attn_strerror(code)
         assert msg and msg != "unknown status"
-    assert binding.attn_strerror(-11) == "unknown status"
+    assert binding.attn_strerror(-13) == "unknown status"
     assert binding.attn_strerror(-10).startswith("HIP error")
     s = binding.attn_decode_auto_splits(16, 32, 32768, 128)
     assert 1 <= s <= binding.ATTN_MAX_SPLITS

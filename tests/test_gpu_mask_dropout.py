@@ -1,0 +1,158 @@
+"""GPU parity of the fused general mask and dropout (``attn_fwd_ex``,
+``attn_bwd_ex``) against the float64 oracle (``attention_ex``,
+``attention_ex_bwd``) on the same rounded inputs.
+
+Masks are seeded (boolean with some rows left without any key, additive
+with -inf entries), broadcast over batch or heads; dropout uses Philox4x32-10
+on both sides, and one case reads the keep pattern back bit for bit (V = I
+makes O_ij = P_ij Z_ij / (1 - p), so the dropped weights are exact zeros).
+Bounds: forward as for the plain forward (max |dO| 1e-2 fp16, 2e-2 bf16;
+LSE within 1e-4 * max(1, |LSE_ref|); rows without keys exactly O = 0,
+LSE = -inf); backward max |x - x_ref| <= 4 u max |x_ref| (u = 2^-8 bf16,
+2^-11 fp16) as for the plain backward.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from io_aware_softmax_amd import inputs
+from tests.gpu_common import O_TOL, compare, require_gpu, say, to_device, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+TAU = {"bf16": 4 * 2.0 ** -8, "f16": 4 * 2.0 ** -11}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import io_aware_softmax_amd as m
+    m.load()
+    yield
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _mask_tensor(mask):
+    import torch
+    if mask is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+
+
+def _case(name, B, H, Lq, Lk, D, dtype, causal, seed, mask=None, kind=None, p=0.0, dseed=0, offset=0,
+          bwd=True):
+    import torch
+    from io_aware_softmax_amd import binding
+    wl = inputs.custom(name, B, H, Lq, Lk, D, dtype, causal, seed=seed)
+    bits = inputs.generate(wl, ("q", "k", "v", "do"))
+    q, k, v, do = (to_device(bits[t], dtype) for t in ("q", "k", "v", "do"))
+    mt = _mask_tensor(mask)
+    say(f"case {name} B{B} H{H} Lq{Lq} Lk{Lk} D{D} {dtype} causal={causal} mask={kind} "
+        f"{None if mask is None else mask.shape} p={p} seed={dseed} offset={offset}")
+    O, L = binding.attn_fwd_ex(q, k, v, causal=causal, scale=wl.scale, mask=mt, dropout_p=p, seed=dseed,
+                               offset=offset)
+    torch.cuda.synchronize()
+    vals = {t: inputs.to_float32(bits[t], dtype) for t in ("q", "k", "v", "do")}
+    kw = dict(mask=mask, mask_kind=kind, dropout_p=p, seed=dseed, offset=offset)
+    Or, Lr = oracle.attention_ex(vals["q"], vals["k"], vals["v"], wl.scale, causal, **kw)
+    O, L = to_host_f64(O), to_host_f64(L)
+    empty = np.isneginf(Lr)
+    assert np.all(O[empty] == 0) and np.all(np.isneginf(L[empty])), "rows without keys"
+    compare(name, dtype, O[~empty], L[~empty], Or[~empty], Lr[~empty])
+    if not bwd:
+        return
+    O_t, L_t = binding.attn_fwd_ex(q, k, v, causal=causal, scale=wl.scale, mask=mt, dropout_p=p, seed=dseed,
+                                   offset=offset)
+    grads = binding.attn_bwd_ex(q, k, v, O_t, L_t, do, causal=causal, scale=wl.scale, mask=mt, dropout_p=p,
+                                seed=dseed, offset=offset)
+    torch.cuda.synchronize()
+    ref = oracle.attention_ex_bwd(vals["q"], vals["k"], vals["v"], vals["do"], wl.scale, causal, **kw)
+    for tname, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+        g = to_host_f64(g)
+        assert np.all(np.isfinite(g)), f"{name}: non-finite {tname}"
+        scale = float(np.max(np.abs(r)))
+        rel = float(np.max(np.abs(g - r))) / scale if scale > 0 else float(np.max(np.abs(g)))
+        say(f"  {name} {tname}: ratio {rel:.3e} (tol {TAU[dtype]:.2e})")
+        assert rel <= TAU[dtype], f"{name}: {tname} {rel}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bool_mask(dtype, D, causal):
+    B, H, Lq, Lk = 2, 2, 200, 333
+    mask = inputs.bool_mask(10 + D, (1, H, Lq, Lk), keep=0.6, empty_rows=3)
+    _case(f"bool_{dtype}_D{D}_c{int(causal)}", B, H, Lq, Lk, D, dtype, causal, seed=20 + D, mask=mask, kind="bool")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_additive_mask_batch_broadcast(causal):
+    B, H, Lq, Lk = 2, 3, 150, 260
+    mask = inputs.additive_mask(31, (B, 1, Lq, Lk))
+    _case(f"add_c{int(causal)}", B, H, Lq, Lk, 128, "bf16", causal, seed=31, mask=mask, kind="add")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_dropout(dtype, p):
+    _case(f"drop_{dtype}_{p}", 1, 3, 260, 260, 128, dtype, True, seed=40, p=p, dseed=0x1234_5678_9ABC_DEF0, offset=3)
+
+
+def test_mask_and_dropout_together():
+    mask = inputs.additive_mask(51, (1, 1, 130, 400), neg_inf=0.3)
+    _case("add_drop", 2, 2, 130, 400, 64, "bf16", True, seed=51, mask=mask, kind="add", p=0.3, dseed=9, offset=77)
+
+
+def test_all_ones_mask_matches_plain_forward():
+    """The mask kernel with nothing masked against the plain kernels."""
+    import torch
+    from io_aware_softmax_amd import binding
+    wl = inputs.custom("ones", 1, 4, 300, 300, 128, "bf16", True, seed=61)
+    bits = inputs.generate(wl)
+    q, k, v = (to_device(bits[t], "bf16") for t in "qkv")
+    ones = torch.ones((1, 1, 300, 300), dtype=torch.uint8, device="cuda")
+    O1, L1 = binding.attn_fwd_ex(q, k, v, causal=True, mask=ones)
+    O2, L2 = binding.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    say("case all-ones mask vs plain forward")
+    assert (O1.float() - O2.float()).abs().max().item() <= 2 * O_TOL["bf16"]
+    assert ((L1 - L2).abs() / L2.abs().clamp(min=1)).max().item() <= 2e-4
+
+
+def test_dropout_keep_pattern_bit_exact():
+    """V = I (Lk = D = 128): O_ij = P_ij Z_ij / (1 - p), so the zeros of O
+    are exactly the dropped weights; compared with the oracle's Philox."""
+    import torch
+    from io_aware_softmax_amd import binding
+    from oracle import philox
+    B, H, Lq, Lk, D, p = 2, 2, 96, 128, 128, 0.3
+    wl = inputs.custom("keep_bits", B, H, Lq, Lk, D, "bf16", False, seed=71)
+    bits = inputs.generate(wl, ("q", "k"))
+    q, k = (to_device(bits[t], "bf16") for t in "qk")
+    v = torch.eye(D, dtype=torch.bfloat16, device="cuda").expand(B, H, Lk, D).contiguous()
+    for seed, offset in ((5, 0), (2 ** 40 + 3, 12345)):
+        O, _ = binding.attn_fwd_ex(q, k, v, dropout_p=p, seed=seed, offset=offset)
+        torch.cuda.synchronize()
+        got = (O.float().cpu().numpy() != 0)
+        say(f"case keep pattern seed={seed} offset={offset}")
+        for b in range(B):
+            for h in range(H):
+                ref = philox.keep_pattern(seed, offset, b * H + h, np.arange(Lq), Lk, p)
+                assert np.array_equal(got[b, h], ref), (b, h)
+
+
+def test_ex_deterministic_and_offset_sensitive():
+    import torch
+    from io_aware_softmax_amd import binding
+    wl = inputs.custom("det_ex", 1, 4, 256, 256, 128, "bf16", True, seed=81)
+    bits = inputs.generate(wl)
+    q, k, v = (to_device(bits[t], "bf16") for t in "qkv")
+    a, _ = binding.attn_fwd_ex(q, k, v, causal=True, dropout_p=0.2, seed=1, offset=0)
+    b, _ = binding.attn_fwd_ex(q, k, v, causal=True, dropout_p=0.2, seed=1, offset=0)
+    c, _ = binding.attn_fwd_ex(q, k, v, causal=True, dropout_p=0.2, seed=1, offset=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert not torch.equal(a, c)
