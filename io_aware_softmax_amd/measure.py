@@ -13,6 +13,9 @@ Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
   L = 8192, bf16 D128 lengths causal and not, one sequence with one or a few
   heads (few workgroups), and chunked prefill (Lq new queries against Lk
   cached keys).  One JSON line per case.
+* ``ex`` - forward and backward of the causal bf16 8k prefill through the
+  plain entry points and through attn_fwd_ex / attn_bwd_ex with boolean and
+  additive masks and dropout.  One JSON line per case.
 * ``sweep`` - the fp16 length sweep (B4 H8 D64, L = 64 ... 4096,
   non-causal): TFLOP/s of ``attn_fwd`` next to a materialised-softmax GPU
   baseline that writes the scores and weights to device memory (the naive
@@ -168,16 +171,51 @@ def cmd_sweep_ext(args):
         torch.cuda.empty_cache()
 
 
+def cmd_ex(args):
+    """Forward and backward of the causal bf16 prefill shape (B1 H32 L8192
+    D128) through the plain entry points and through the general ones with a
+    boolean mask (broadcast over heads, half the keys of every row kept),
+    an additive mask, dropout 0.1, and mask plus dropout.  Flops are the
+    algorithmic ones of the causal problem (forward 4 D per allowed pair,
+    backward 2.5 times that) whatever the mask removes."""
+    wl = inputs.WORKLOADS["causal_bf16_8k"]
+    q, k, v = _upload(wl)
+    g = _dev(inputs.generate(wl, ("do",))["do"], wl.dtype)
+    L = wl.Lq
+    bmask = torch.from_numpy(inputs.bool_mask(5, (1, 1, L, L), keep=0.5)).cuda()
+    amask = torch.from_numpy(inputs.additive_mask(6, (1, 1, L, L), neg_inf=0.0)).cuda()
+    cases = [("plain", None, 0.0), ("bool mask", bmask, 0.0), ("additive mask", amask, 0.0),
+             ("dropout 0.1", None, 0.1), ("bool mask + dropout 0.1", bmask, 0.1)]
+    for label, mask, p in cases:
+        if label == "plain":
+            fwd = lambda: binding.attn_fwd(q, k, v, causal=True, scale=wl.scale)
+        else:
+            fwd = lambda: binding.attn_fwd_ex(q, k, v, causal=True, scale=wl.scale, mask=mask, dropout_p=p, seed=3)
+        O, Lse = fwd()
+        if label == "plain":
+            bwd = lambda: binding.attn_bwd(q, k, v, O, Lse, g, causal=True, scale=wl.scale)
+        else:
+            bwd = lambda: binding.attn_bwd_ex(q, k, v, O, Lse, g, causal=True, scale=wl.scale, mask=mask,
+                                              dropout_p=p, seed=3)
+        tf = _time(fwd, args.reps)
+        tb = _time(bwd, args.reps)
+        rec = {"case": label, "workload": wl.name, "fwd_ms": tf[0], "fwd_tflops": wl.flops() / tf[0] / 1e9,
+               "bwd_ms": tb[0], "bwd_tflops": 2.5 * wl.flops() / tb[0] / 1e9,
+               "mask_bytes": 0 if mask is None else mask.numel() * mask.element_size()}
+        print(json.dumps(rec), flush=True)
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    p.add_argument("cmd", choices=["kernels", "copy", "sweep", "sweep_ext"])
+    p.add_argument("cmd", choices=["kernels", "copy", "sweep", "sweep_ext", "ex"])
     p.add_argument("--reps", type=int, default=5)
     args = p.parse_args(argv)
     if not torch.cuda.is_available():
         print("needs a GPU", file=sys.stderr)
         return 1
     binding.load()
-    {"kernels": cmd_kernels, "copy": cmd_copy, "sweep": cmd_sweep, "sweep_ext": cmd_sweep_ext}[args.cmd](args)
+    {"kernels": cmd_kernels, "copy": cmd_copy, "sweep": cmd_sweep, "sweep_ext": cmd_sweep_ext,
+     "ex": cmd_ex}[args.cmd](args)
     return 0
 
 
