@@ -156,3 +156,50 @@ def test_ex_deterministic_and_offset_sensitive():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert not torch.equal(a, c)
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,kind,mshape,p,scale", [
+    (2, 3, 1, 1000, 128, "bf16", False, "bool", "full", 0.25, None),      # one query per (b, h)
+    (2, 2, 77, 77, 64, "f16", True, "add", "full", 0.0, -0.3),            # negative scale, full mask
+    (1, 2, 300, 130, 64, "f16", False, "add", "heads", 0.4, None),        # Lq > Lk
+    (3, 2, 65, 129, 128, "bf16", True, "bool", "batch", 0.05, None),      # tile + 1 on both sides
+])
+def test_ex_edge_shapes(B, H, Lq, Lk, D, dtype, causal, kind, mshape, p, scale):
+    shape = {"full": (B, H, Lq, Lk), "heads": (1, H, Lq, Lk), "batch": (B, 1, Lq, Lk)}[mshape]
+    if kind == "bool":
+        mask = inputs.bool_mask(Lq + Lk, shape, keep=0.7, empty_rows=1)
+    else:
+        mask = inputs.additive_mask(Lq + Lk, shape, neg_inf=0.2)
+    name = f"edge_{Lq}x{Lk}_D{D}_{dtype}_{kind}_{mshape}_p{p}"
+    if scale is None:
+        _case(name, B, H, Lq, Lk, D, dtype, causal, seed=Lq * 7 + Lk, mask=mask, kind=kind, p=p,
+              dseed=(1 << 63) | 12345, offset=0xFFFFFFFF)
+    else:
+        _case_scaled(name, B, H, Lq, Lk, D, dtype, causal, Lq * 7 + Lk, mask, kind, p, scale)
+
+
+def _case_scaled(name, B, H, Lq, Lk, D, dtype, causal, seed, mask, kind, p, scale):
+    """As _case with an explicit scale (forward and backward)."""
+    import torch
+    from io_aware_softmax_amd import binding
+    wl = inputs.custom(name, B, H, Lq, Lk, D, dtype, causal, seed=seed)
+    bits = inputs.generate(wl, ("q", "k", "v", "do"))
+    q, k, v, do = (to_device(bits[t], dtype) for t in ("q", "k", "v", "do"))
+    mt = _mask_tensor(mask)
+    say(f"case {name} scale={scale}")
+    O, L = binding.attn_fwd_ex(q, k, v, causal=causal, scale=scale, mask=mt, dropout_p=p, seed=4)
+    grads = binding.attn_bwd_ex(q, k, v, O, L, do, causal=causal, scale=scale, mask=mt, dropout_p=p, seed=4)
+    torch.cuda.synchronize()
+    vals = {t: inputs.to_float32(bits[t], dtype) for t in ("q", "k", "v", "do")}
+    kw = dict(mask=mask, mask_kind=kind, dropout_p=p, seed=4)
+    Or, Lr = oracle.attention_ex(vals["q"], vals["k"], vals["v"], scale, causal, **kw)
+    O, L = to_host_f64(O), to_host_f64(L)
+    empty = np.isneginf(Lr)
+    assert np.all(O[empty] == 0) and np.all(np.isneginf(L[empty]))
+    compare(name, dtype, O[~empty], L[~empty], Or[~empty], Lr[~empty])
+    ref = oracle.attention_ex_bwd(vals["q"], vals["k"], vals["v"], vals["do"], scale, causal, **kw)
+    for tname, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+        g = to_host_f64(g)
+        rel = float(np.max(np.abs(g - r))) / max(float(np.max(np.abs(r))), 1e-30)
+        say(f"  {name} {tname}: ratio {rel:.3e} (tol {TAU[dtype]:.2e})")
+        assert rel <= TAU[dtype], f"{name}: {tname} {rel}"
