@@ -51,11 +51,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kRun = 2;             // DMA instructions per M0 run
-constexpr int kDmaWaves = 4;        // group 1 issues the DMA
-// Largest lag (base 2) of the reference maximum behind the true running
-// maximum: weights exp(a - d) stay below 2^8.
-constexpr float kTau = 8.f;
-constexpr float kTauWeight = 256.f;  // 2^kTau
+constexpr int kDmaWaves = 4;        // the 4 waves of group 0 issue the DMA
+// Largest weight exp(a - d) of the common path: 2^8 (the reference maximum
+// may lag the true running maximum by up to 8, base 2).
+constexpr float kTauWeight = 256.f;
 // Headroom (base 2) of a new reference above the tile maximum that set it.
 // bf16 weights keep the fp32 exponent range, so a reference 24 above the
 // maximum (weights down to 2^-24 at first) costs no precision and makes
@@ -352,8 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // the diagonal get score -inf and so weight exp2(-inf) = 0 (the scale is
   // positive here).  The weights are first taken against the current
   // reference d.  Every weight of a lane is at most that lane's sum, so when
-  // no sum exceeds 2^kTau (and every row has a reference) the weights stay
-  // within 2^kTau and the reference may stay.  Otherwise (a maximum jumped,
+  // no sum exceeds 2^8 (and every row has a reference) the weights stay
+  // within 2^8 and the reference may stay.  Otherwise (a maximum jumped,
   // or an exponential overflowed to inf) the tile maximum is taken, the
   // reference advanced and the weights recomputed; the scores are still in
   // sc.  A tile this wave does not compute gets zero weights.
@@ -393,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       // with headroom: a row whose tile maximum passed its reference moves
       // the reference kHeadroom above that maximum and corrects O~ and s by
       // exp(d_old - d_new); exact for any reference, and later tiles may
-      // rise kHeadroom + kTau before they come back here.
+      // rise kHeadroom + 8 before they come back here.
       const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
       const bool grow = m_tile > m_ref;
       const float m_new = grow ? m_tile + kHeadroom<BF16> : m_ref;
