@@ -321,25 +321,63 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       *reinterpret_cast<float4*>(dd + 8 * hh + 4) = *reinterpret_cast<const float4*>(st + BQ + base + 4);
     }
     const bool masked = CAUSAL && qb + off < kw0 + 31;
+    // Mask terms (base 2) of the 16 elements: branch-free loads (elements
+    // outside [0, Lq) x [0, Lk) read element (0, 0) of the slab and get 0).
+    float mt[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt[r] = 0.f;
+    if constexpr (EX) {
+      if (md.kind != 0) {
+        size_t idx[16];
+        bool in[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+          in[r] = qi < Lq && key < Lk;
+          idx[r] = mslab + (in[r] ? (size_t)qi * Lk + key : 0);
+        }
+        if (md.kind == 1) {
+          const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
+          unsigned char v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = m8[idx[r]];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt[r] = (in[r] && v[r] == 0) ? -INFINITY : 0.f;
+        } else {
+          const float* m32 = static_cast<const float*>(md.mask);
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = m32[idx[r]];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt[r] = in[r] ? v[r] * kLog2e : 0.f;
+        }
+      }
+    }
+    // Dropout keep bits of the 16 elements (bit r), one Philox block each.
+    unsigned kbits = 0xFFFFu;
+    if constexpr (EX) {
+      if (md.dropout) {
+        kbits = 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+          kbits |= (dropout_keep1(pk, key, qi, bh, md.offset, md.thr) ? 1u : 0u) << r;
+        }
+      }
+    }
     s16x8 pa[2], sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-      float mt = 0.f;  // mask term (base 2)
-      if constexpr (EX) {
-        if (md.kind != 0 && qi < Lq && key < Lk) mt = mask_term(md, mslab + (size_t)qi * Lk + key);
-      }
-      float p = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt - l2[r]));
+      float p = mt[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt[r] - l2[r]));
       if (masked && key > qi + off) p = 0.f;
       // Dropout: the value product sees the kept weights scaled by 1/(1-p),
       // and dP reaches the softmax through the same factors.
       float pv = p, dpk = dp[r];
       if constexpr (EX) {
-        if (md.dropout) {
-          const bool kp = dropout_keep1(pk, key, qi, bh, md.offset, md.thr);
-          pv = kp ? p * md.rp : 0.f;
-          dpk = kp ? dpk * md.rp : 0.f;
-        }
+        const float z = ((kbits >> r) & 1u) ? md.rp : 0.f;  // md.rp = 1 without dropout
+        pv = p * z;
+        dpk = dpk * z;
       }
       const float ds = p * (dpk - dd[r]);
       pa[r >> 3][r & 7] = (short)round16<BF16>(pv);
