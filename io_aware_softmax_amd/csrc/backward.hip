@@ -599,7 +599,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int key0 = kb0 + 16 * half + 8 * h;
-        if (md.kind != 0) mask_terms8(md, mrow + key0, key0, Lk, *reinterpret_cast<float(*)[8]>(mt + 8 * half));
+        if (md.kind != 0)
+          mask_terms8(md, mrow + key0, key0, Lk, Lk % 8 == 0 && kb0 + 32 <= Lk,
+                      *reinterpret_cast<float(*)[8]>(mt + 8 * half));
         if (md.dropout) keep[half] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
       }
     }

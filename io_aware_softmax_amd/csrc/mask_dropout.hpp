@@ -22,24 +22,19 @@ __device__ __forceinline__ size_t mask_slab(const MaskDropout& md, int bh, int L
   return (size_t)slab * Lq * Lk;
 }
 
-// Base-2 additive term of one element (idx = slab + i Lk + j): 0 / -inf for
-// a boolean mask, bias * log2(e) for an additive one, 0 without a mask.
-__device__ __forceinline__ float mask_term(const MaskDropout& md, size_t idx) {
-  if (md.kind == 1) return static_cast<const unsigned char*>(md.mask)[idx] ? 0.f : -INFINITY;
-  if (md.kind == 2) return static_cast<const float*>(md.mask)[idx] * kLog2e;
-  return 0.f;
-}
-
 // Terms of keys j0 .. j0 + 7 of one query row (idx = slab + i Lk + j0);
-// keys at or past Lk get -inf.  One 8-byte (boolean) or two 16-byte
-// (additive) loads when the 8 keys are inside the row and aligned.
-__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, float (&t)[8]) {
+// keys at or past Lk get -inf.  `vec` (wave-uniform: Lk % 8 == 0 and all
+// 8 keys before Lk) selects one 8-byte (boolean) or two 16-byte (additive)
+// loads; otherwise 8 element loads, each from an index clamped into the row
+// so that no load depends on a lane condition.
+__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
+                                            float (&t)[8]) {
   if (md.kind == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? 0.f : -INFINITY;
     return;
   }
-  if (j0 + 8 <= Lk && idx % 8 == 0) {
+  if (vec) {
     if (md.kind == 1) {
       const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + idx);
 #pragma unroll
@@ -52,8 +47,24 @@ __device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, i
     }
     return;
   }
+  size_t ie[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? mask_term(md, idx + e) : -INFINITY;
+  for (int e = 0; e < 8; ++e) ie[e] = j0 + e < Lk ? idx + e : idx - j0;  // key 0 of the row: in bounds
+  if (md.kind == 1) {
+    const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
+    unsigned char v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = m8[ie[e]];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (j0 + e < Lk && v[e] != 0) ? 0.f : -INFINITY;
+  } else {
+    const float* m32 = static_cast<const float*>(md.mask);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = m32[ie[e]];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? v[e] * kLog2e : -INFINITY;
+  }
 }
 
 }  // namespace attn

@@ -125,12 +125,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     // Register r of block b holds key kv0 + 32 b + 16 (r / 8) + 8 h + r % 8.
     float mx = -INFINITY;
     unsigned keep[4] = {0xffu, 0xffu, 0xffu, 0xffu};
+    const bool vec = Lk % 8 == 0 && kv0 + BQ <= Lk;  // whole, aligned mask rows for the tile
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int b = grp >> 1, half = grp & 1;
       const int key0 = kv0 + 32 * b + 16 * half + 8 * h;
       float t8[8];
-      mask_terms8(md, mrow + key0, key0, Lk, t8);
+      mask_terms8(md, mrow + key0, key0, Lk, vec, t8);
       if (md.dropout) keep[grp] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
