@@ -114,6 +114,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     if (kv0 >= w_key_end) return;
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
+    // Mask terms of the tile's 32 keys, loaded before the score products so
+    // that the loads overlap them.
+    const bool vec = Lk % 8 == 0 && kv0 + BQ <= Lk;  // whole, aligned mask rows for the tile
+    float t8[4][8];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
+      mask_terms8(md, mrow + key0, key0, Lk, vec, t8[grp]);
+    }
     f32x16 s[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -125,18 +134,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     // Register r of block b holds key kv0 + 32 b + 16 (r / 8) + 8 h + r % 8.
     float mx = -INFINITY;
     unsigned keep[4] = {0xffu, 0xffu, 0xffu, 0xffu};
-    const bool vec = Lk % 8 == 0 && kv0 + BQ <= Lk;  // whole, aligned mask rows for the tile
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int b = grp >> 1, half = grp & 1;
       const int key0 = kv0 + 32 * b + 16 * half + 8 * h;
-      float t8[8];
-      mask_terms8(md, mrow + key0, key0, Lk, vec, t8);
       if (md.dropout) keep[grp] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * half + e;
-        float x = __builtin_fmaf(s[b][r], c, t8[e]);
+        float x = __builtin_fmaf(s[b][r], c, t8[grp][e]);
         if (CAUSAL && key0 + e > qi + off) x = -INFINITY;
         s[b][r] = x;
         mx = fmaxf(mx, x);
