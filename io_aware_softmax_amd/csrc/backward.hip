@@ -353,15 +353,35 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
         }
       }
     }
-    // Dropout keep bits of the 16 elements (bit r), one Philox block each.
+    // Dropout keep bits of the 16 elements (bit r).  Element r needs word
+    // (key mod 4) of the Philox block of (key / 4, query of r); the 4 lanes of
+    // a quad hold keys 4m .. 4m+3 of one half-wave and need the same 16
+    // blocks.  Lane u of the quad computes the blocks of r = 4 t + u, and the
+    // quad exchanges words with DPP quad permutations: in rotation k, lane v
+    // offers word (v + k) mod 4 of its block and lane u takes it from lane
+    // (u - k) mod 4 -- word u of the block of r = 4 t + ((u - k) mod 4).
     unsigned kbits = 0xFFFFu;
     if constexpr (EX) {
       if (md.dropout) {
         kbits = 0u;
+        const int u = n & 3;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * t + u;
           const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-          kbits |= (dropout_keep1(pk, key, qi, bh, md.offset, md.thr) ? 1u : 0u) << r;
+          const uint4 wd = philox4x32_10(make_uint4((unsigned)key >> 2, (unsigned)qi, (unsigned)bh, md.offset), pk);
+          const unsigned wv[4] = {wd.x, wd.y, wd.z, wd.w};
+          static_for<4>([&](auto K) __attribute__((always_inline)) {
+            constexpr int k = decltype(K)::value;
+            const int sel = (u + k) & 3;
+            const unsigned offer = sel == 0 ? wv[0] : sel == 1 ? wv[1] : sel == 2 ? wv[2] : wv[3];
+            // quad_perm control: lane u reads lane (u - k) mod 4
+            constexpr int kPerm = ((0 - k) & 3) | (((1 - k) & 3) << 2) | (((2 - k) & 3) << 4) | (((3 - k) & 3) << 6);
+            unsigned got = offer;
+            if constexpr (k != 0) got = (unsigned)__builtin_amdgcn_mov_dpp((int)offer, kPerm, 0xF, 0xF, false);
+            const int rr = 4 * t + ((u - k) & 3);
+            kbits |= (got >= md.thr ? 1u : 0u) << rr;
+          });
         }
       }
     }
