@@ -165,9 +165,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         pb[grp][e] = (short)round16<BF16>(((keep[grp] >> e) & 1u) ? p : 0.f);
       }
     }
-    l_run = l_run * alpha + psum;
+    // The correction exp(d_old - d_new) is 1 unless a row's maximum moved
+    // (or this is its first key): skip the multiplications when no row of
+    // the wave needs them.
+    if (__any(alpha != 1.f)) {
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    l_run += psum;
     // O^T += V^T P^T over the tile's four 16-key k-steps.
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
