@@ -57,3 +57,30 @@ def test_named_workloads():
     assert w["decode_bf16_32k"].kv_bytes() == 8589934592
     assert w["long_causal_bf16_64k"].flops() == pytest.approx(8.796e12, rel=1e-3)
     assert w["check_f32"].scale == 0.125
+
+
+def test_upstream_gradient_draws():
+    """dO has the queries' shape, its own stream (tensor id 3) and regenerates
+    slab by slab."""
+    wl = inputs.custom("do_draw", 2, 3, 17, 29, 64, "bf16", True, seed=5)
+    a = inputs.generate(wl, ("q", "do"))
+    assert a["do"].shape == (2, 3, 17, 64)
+    assert not np.array_equal(a["do"], a["q"])
+    b = inputs.generate(wl, ("do",))
+    np.testing.assert_array_equal(a["do"], b["do"])
+    np.testing.assert_array_equal(a["do"][1, 2], inputs.slab(wl.seed_words, "do", 1, 2, 17, 64, "bf16"))
+
+
+def test_mask_generators():
+    m = inputs.bool_mask(3, (2, 1, 50, 70), keep=0.6, empty_rows=4)
+    assert m.dtype == np.uint8 and m.shape == (2, 1, 50, 70)
+    assert np.all(m[0, 0, :4] == 0)
+    assert abs(m[:, :, 4:].mean() - 0.6) < 0.03
+    np.testing.assert_array_equal(m, inputs.bool_mask(3, (2, 1, 50, 70), keep=0.6, empty_rows=4))
+    a = inputs.additive_mask(4, (1, 2, 40, 60), sigma=2.0, neg_inf=0.1)
+    assert a.dtype == np.float32
+    frac = np.isneginf(a).mean()
+    assert 0.05 < frac < 0.15
+    fin = a[np.isfinite(a)]
+    assert abs(fin.std() - 2.0) < 0.15
+    np.testing.assert_array_equal(a, inputs.additive_mask(4, (1, 2, 40, 60), sigma=2.0, neg_inf=0.1))
