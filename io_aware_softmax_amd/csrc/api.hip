@@ -3,6 +3,7 @@
 // contract are in include/attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -64,6 +65,20 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 int prefill_variant() {
   const char* e = std::getenv("ATTN_PREFILL_KERNEL");
   return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
+}
+
+// Key-range count of the two-group prefill: ATTN_PREFILL_SPLITS=n forces
+// n (1 = never split; capped so that no range is empty), else the library
+// chooses from the shape and the device's compute-unit count.
+hipError_t prefill_splits(int BH, int Lq, int Lk, bool causal, int* out) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const char* env = std::getenv("ATTN_PREFILL_SPLITS");
+  const int forced = (env != nullptr && *env != '\0') ? std::max(1, std::atoi(env)) : 0;
+  *out = attn::prefill_pp_auto_splits(BH, Lq, Lk, causal, cus, forced);
+  return hipSuccess;
 }
 
 int auto_splits(int64_t BH, int Lk) {
@@ -228,12 +243,31 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
   // D = 64 (softmax-bound: half the products per score) and scale 0 (whose
   // masked keys need explicit zero weights) take the single-group kernel.
   hipError_t e;
-  if (dtype == ATTN_F32)
+  if (dtype == ATTN_F32) {
     e = attn::launch_prefill_f32(D, causal != 0, a, s);
-  else if (D == 128 && a.c > 0.f && prefill_variant() != 1)
-    e = attn::launch_prefill_pp(dtype, causal != 0, a, s);
-  else
+  } else if (D == 128 && a.c > 0.f && prefill_variant() != 1) {
+    // Shapes with fewer query tiles than the part has compute units (one
+    // head, short chunks) cut each tile's keys into ranges, merged after.
+    int n_split = 1;
+    e = prefill_splits(a.BH, Lq, Lk, causal != 0, &n_split);
+    if (e != hipSuccess) return hip_fail(e);
+    if (n_split > 1) {
+      const size_t rows = size_t(a.BH) * Lq;
+      const size_t bytes = size_t(n_split) * rows * (size_t(D) + 1) * sizeof(float);
+      void* ws = nullptr;
+      e = hipMallocAsync(&ws, bytes, s);
+      if (e != hipSuccess) return hip_fail(e);
+      float* part_o = static_cast<float*>(ws);
+      e = attn::launch_prefill_pp_split(dtype, causal != 0, a, n_split, part_o, part_o + size_t(n_split) * rows * D,
+                                        s);
+      const hipError_t ef = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = ef;
+    } else {
+      e = attn::launch_prefill_pp(dtype, causal != 0, a, s);
+    }
+  } else {
     e = attn::launch_prefill_mfma(dtype, D, causal != 0, a, s);
+  }
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

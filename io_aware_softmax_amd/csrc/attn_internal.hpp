@@ -82,6 +82,14 @@ hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out)
 hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Two-group (ping-pong) variant of the 16-bit prefill for D = 128.
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
+// The same with every query tile's keys cut into n_split ranges (partials in
+// part_o [n_split, BH, Lq, 128] and part_l [n_split, BH, Lq] fp32), then merged.
+hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, int n_split, float* part_o,
+                                   float* part_l, hipStream_t s);
+// Key-range count for launch_prefill_pp_split on a part with `cus` compute
+// units (1: do not split): only shapes with fewer than cus / 2 query tiles.
+// forced > 0 asks for that count, capped so that no range is empty.
+int prefill_pp_auto_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced);
 // The same algorithm with fp32 inputs on the fp32 MFMA.
 hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Forward with a general mask and / or dropout (16-bit dtypes).

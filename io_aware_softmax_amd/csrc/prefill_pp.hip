@@ -129,11 +129,16 @@ __device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbas
   }
 }
 
-template <bool BF16, int D, bool CAUSAL>
+// SPLIT: every (batch*head, query tile) is cut into n_split contiguous key
+// ranges, each an item of its own; an item writes its rows' normalised
+// partial output and log-sum-exp (part_o, part_l) instead of O and LSE, and
+// prefill_split_combine merges them.
+template <bool BF16, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE, int BH,
-    int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd) {
+    int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd, int n_split,
+    float* __restrict__ part_o, float* __restrict__ part_l) {
   using T = Tile<D>;
   using LY = Layout<D>;
   using KP = DmaPlan<T::KINST, kRun, kDmaWaves>;
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // tiles with light ones); a workgroup with several items runs them one
   // after the other and loads the next item's first tiles and Q while it
   // writes the current output.
-  const int total = BH * nqt;
+  const int total = BH * nqt * (SPLIT ? n_split : 1);
   const int wg = blockIdx.x;
   const int xcd = wg % 8, slot = wg / 8;
   const int range_lo = xcd * items_per_xcd;
@@ -176,12 +181,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
 
   // Per-item values (wave-uniform ones in SGPRs).
   int bh = 0, nkv = 0, wq0 = 0, w_nkv = 0, j_mask = 0, qi = 0;
+  int jl_s = 0, sp_s = 0;  // SPLIT: first key tile of the item's range, range index
   const char* Kb = nullptr;
   const char* Vb = nullptr;
   s16x8 qreg[T::KSTEPS];
   auto setup = [&](int logical) __attribute__((always_inline)) {
-    bh = logical / nqt;
-    const int qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
+    int tile_item = logical;
+    if constexpr (SPLIT) {
+      sp_s = logical % n_split;
+      tile_item = logical / n_split;
+    }
+    bh = tile_item / nqt;
+    const int qt = CAUSAL ? nqt - 1 - tile_item % nqt : tile_item % nqt;
     const int q0 = qt * kRows;
     Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
     Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
@@ -200,6 +211,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     }
     if (Lk % BN) jm = min(jm, Lk / BN);
     j_mask = __builtin_amdgcn_readfirstlane(jm);
+    if constexpr (SPLIT) {
+      // Key tiles [jl, jh) of the query tile's [0, nkv), balanced so that no
+      // range is empty (the launch keeps n_split <= every tile's nkv); the
+      // counts below become local to that range.
+      const int jl = sp_s * nkv / n_split;
+      const int jh = (sp_s + 1) * nkv / n_split;
+      jl_s = __builtin_amdgcn_readfirstlane(jl);
+      nkv = __builtin_amdgcn_readfirstlane(jh - jl);
+      w_nkv = __builtin_amdgcn_readfirstlane(max(0, min(w_nkv - jl, nkv)));
+      j_mask = __builtin_amdgcn_readfirstlane(max(0, min(j_mask - jl, nkv)));
+    }
     // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
     qi = wq0 + n;
     const unsigned short* Qh = Q + (size_t)bh * Lq * D;
@@ -225,7 +247,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   auto biased = [](const char* p) __attribute__((always_inline)) {
     return reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) - kDmaBias);
   };
+  // kv0 arguments are local to the item's key range (SPLIT adds its start).
   auto dma_k = [&](char* buf, int kv0) __attribute__((always_inline)) {
+    if constexpr (SPLIT) kv0 += jl_s * BN;
     const char* g = biased(Kb + (size_t)kv0 * (D * 2));
     if (kv0 + BN <= Lk)
       dma_tile_whole<KP>(g, buf, k_src, wd);
@@ -233,6 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       dma_tile_ragged<D, KP>(g, buf, k_src, wd, Lk - kv0);
   };
   auto dma_v = [&](char* buf, int kv0) __attribute__((always_inline)) {
+    if constexpr (SPLIT) kv0 += jl_s * BN;
     const char* g = biased(Vb + (size_t)kv0 * (D * 2));
     if (kv0 + BN <= Lk)
       dma_tile_whole<VP>(g, buf, v_src, wd);
@@ -241,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   };
   // Wait for this wave's DMA; zero the V slots of rows past Lk it filled.
   auto land = [&](char* vbuf, int kv0) __attribute__((always_inline)) {
+    if constexpr (SPLIT) kv0 += jl_s * BN;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (vbuf != nullptr && kv0 + BN > Lk) {
 #pragma unroll
@@ -313,9 +339,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   auto matrix = [&](int j, auto issue_tag) __attribute__((always_inline)) {
     constexpr int ISSUE = decltype(issue_tag)::value;
     if constexpr (ISSUE == 1) {
+      const int jg = SPLIT ? j + jl_s : j;  // tile index in the head
       matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc,
-                                        dma_hook(biased(Kb + (size_t)(j + 2) * BN * (D * 2)), kb(j + 2),
-                                                 biased(Vb + (size_t)(j + 1) * BN * (D * 2)), vb(j + 1)));
+                                        dma_hook(biased(Kb + (size_t)(jg + 2) * BN * (D * 2)), kb(j + 2),
+                                                 biased(Vb + (size_t)(jg + 1) * BN * (D * 2)), vb(j + 1)));
     } else {
       if constexpr (ISSUE == 2) {
         if (j + 2 < nkv) dma_k(kb(j + 2), (j + 2) * BN);
@@ -367,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       // bounds are not hoisted out of the tile loop (registers).
       int hk = 8 * h, q = qi;
       asm volatile("" : "+v"(hk), "+v"(q));
-      const int kv0 = t * BN;
+      const int kv0 = (SPLIT ? t + jl_s : t) * BN;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -442,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       softmax_tile(0);
       barrier_lds();
       // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
-      const int j_spread = max(0, min(nkv - 2, Lk / BN - 2));
+      const int j_spread = max(0, min(nkv - 2, Lk / BN - 2 - (SPLIT ? jl_s : 0)));
       int j = 0;
       for (; j < j_spread; ++j) {
         __builtin_amdgcn_s_setprio(1);
@@ -478,6 +505,32 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     }
     __builtin_amdgcn_s_setprio(0);
 
+    if constexpr (SPLIT) {
+      // ---- epilogue of a key range: normalised partial O and its
+      //      log-sum-exp (-inf, with O = 0, for a row with no key in it) ----
+      const float l_tot = halves_sum(l_run);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (qi < Lq) {
+        const size_t prow_ix = ((size_t)sp_s * BH + bh) * Lq + qi;
+        float* po = part_o + prow_ix * D;
+#pragma unroll
+        for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<float4*>(po + 32 * db + 8 * jj + 4 * h) =
+                make_float4(oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                            oacc[db][4 * jj + 3] * inv);
+        if (h == 0) part_l[prow_ix] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+      logical = item_at(++round);
+      if (logical < 0) break;
+      setup(logical);
+      if (grp == 0) {
+        first_tiles();
+        land(vb(0), 0);
+      }
+      continue;
+    }
     // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
     // Each wave stages its 32 rows of O in LDS so that the global stores are
     // whole 16-byte chunks of consecutive rows; the next item's first tiles
@@ -517,17 +570,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   }
 }
 
-template <bool BF16, bool CAUSAL>
-hipError_t launch(const PrefillArgs& a, hipStream_t s) {
+template <bool BF16, bool CAUSAL, bool SPLIT>
+hipError_t launch(const PrefillArgs& a, hipStream_t s, int n_split, float* part_o, float* part_l) {
   const int nqt = (a.Lq + kRows - 1) / kRows;
   const unsigned qsign = a.neg ? 0x80008000u : 0u;
-  const int total = a.BH * nqt;
+  const int total = a.BH * nqt * (SPLIT ? n_split : 1);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   int resident = 0;
-  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_pp_kernel<BF16, 128, CAUSAL>), kThreads,
-                          &resident);
+  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_pp_kernel<BF16, 128, CAUSAL, SPLIT>),
+                          kThreads, &resident);
   if (e != hipSuccess) return e;
   const int cap = resident / 8 * 8;
   int grid, slots, per;
@@ -544,18 +597,91 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s) {
     slots = 0;
     per = 0;
   }
-  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
                      static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse, a.BH, a.Lq,
-                     a.Lk, nqt, a.c, qsign, slots, per);
+                     a.Lk, nqt, a.c, qsign, slots, per, n_split, part_o, part_l);
   return hipGetLastError();
+}
+
+// Merge of the key ranges of a split prefill, one row of D = 128 per 128
+// threads: with lse_p the ranges' log-sum-exps and m = max_p lse_p,
+// O = sum_p exp(lse_p - m) O_p / sum_p exp(lse_p - m) and
+// LSE = m + ln sum_p exp(lse_p - m) -- the guide's output correction with a
+// key range as the chunk (ranges without a key, lse_p = -inf, drop out).
+template <bool BF16>
+__global__ __launch_bounds__(256) void prefill_split_combine(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_l,
+                                                             unsigned short* __restrict__ O, float* __restrict__ LSE,
+                                                             int rows, int n_split) {
+  const int row = blockIdx.x * 2 + (threadIdx.x >> 7);  // (b h) * Lq + q
+  const int d = threadIdx.x & 127;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int p = 0; p < n_split; ++p) m = fmaxf(m, part_l[(size_t)p * rows + row]);
+  float acc = 0.f, wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int p = 0; p < n_split; ++p) {
+      const float lp = part_l[(size_t)p * rows + row];
+      const float wp = lp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lp - m) * kLog2e);
+      wsum += wp;
+      acc = __builtin_fmaf(wp, part_o[((size_t)p * rows + row) * 128 + d], acc);
+    }
+  }
+  O[(size_t)row * 128 + d] = round16<BF16>(wsum > 0.f ? acc / wsum : 0.f);
+  if (d == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s) {
-  if (dtype == 2) return causal ? launch<true, true>(a, s) : launch<true, false>(a, s);
-  return causal ? launch<false, true>(a, s) : launch<false, false>(a, s);
+  if (dtype == 2)
+    return causal ? launch<true, true, false>(a, s, 1, nullptr, nullptr)
+                  : launch<true, false, false>(a, s, 1, nullptr, nullptr);
+  return causal ? launch<false, true, false>(a, s, 1, nullptr, nullptr)
+                : launch<false, false, false>(a, s, 1, nullptr, nullptr);
+}
+
+hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, int n_split, float* part_o,
+                                   float* part_l, hipStream_t s) {
+  hipError_t e;
+  if (dtype == 2)
+    e = causal ? launch<true, true, true>(a, s, n_split, part_o, part_l)
+               : launch<true, false, true>(a, s, n_split, part_o, part_l);
+  else
+    e = causal ? launch<false, true, true>(a, s, n_split, part_o, part_l)
+               : launch<false, false, true>(a, s, n_split, part_o, part_l);
+  if (e != hipSuccess) return e;
+  const int rows = a.BH * a.Lq;
+  if (dtype == 2)
+    prefill_split_combine<true><<<dim3((rows + 1) / 2), dim3(256), 0, s>>>(
+        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, n_split);
+  else
+    prefill_split_combine<false><<<dim3((rows + 1) / 2), dim3(256), 0, s>>>(
+        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, n_split);
+  return hipGetLastError();
+}
+
+int prefill_pp_auto_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced) {
+  const int nqt = (Lq + kRows - 1) / kRows;
+  const long long items = (long long)BH * nqt;
+  // Key tiles of the smallest query tile (every range must be non-empty)
+  // and of the average one (ranges of at least 8 tiles).
+  const int off = Lk - Lq;
+  const int min_nkv = causal ? (min(Lk, min(kRows, Lq) + off) + BN - 1) / BN : (Lk + BN - 1) / BN;
+  if (forced > 0) return max(1, min(forced, min(min_nkv, 16)));
+  if (items * 2 > cus) return 1;
+  long long kv_sum = 0;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int q_last = min((qt + 1) * kRows, Lq) - 1;
+    kv_sum += causal ? (min(Lk, q_last + off + 1) + BN - 1) / BN : (Lk + BN - 1) / BN;
+  }
+  const long long avg_nkv = kv_sum / nqt;
+  long long sp = cus / items;
+  sp = min(sp, (long long)min_nkv);
+  sp = min(sp, avg_nkv / 8);
+  sp = min(sp, 16LL);
+  return sp >= 2 ? (int)sp : 1;
 }
 
 }  // namespace attn
