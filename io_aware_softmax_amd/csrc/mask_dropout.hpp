@@ -22,49 +22,63 @@ __device__ __forceinline__ size_t mask_slab(const MaskDropout& md, int bh, int L
   return (size_t)slab * Lq * Lk;
 }
 
-// Terms of keys j0 .. j0 + 7 of one query row (idx = slab + i Lk + j0);
-// keys at or past Lk get -inf.  `vec` (wave-uniform: Lk % 8 == 0 and all
-// 8 keys before Lk) selects one 8-byte (boolean) or two 16-byte (additive)
-// loads; otherwise 8 element loads, each from an index clamped into the row
-// so that no load depends on a lane condition.
-__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
-                                            float (&t)[8]) {
-  if (md.kind == 0) {
+// Terms of keys j0 .. j0 + 7 of one query row (idx = slab + i Lk + j0) for a
+// mask of kind KIND (0 none, 1 boolean, 2 additive); keys at or past Lk get
+// -inf.  `vec` (wave-uniform: Lk % 8 == 0 and all 8 keys before Lk) selects
+// one 8-byte (boolean) or two 16-byte (additive) loads; otherwise 8 element
+// loads, each from an index clamped into the row so that no load depends on
+// a lane condition.
+template <int KIND>
+__device__ __forceinline__ void mask_terms8_kind(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
+                                                 float (&t)[8]) {
+  if constexpr (KIND == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? 0.f : -INFINITY;
     return;
-  }
-  if (vec) {
-    if (md.kind == 1) {
-      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + idx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = (((e < 4 ? u.x : u.y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx);
-      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx + 4);
-      t[0] = a.x * kLog2e; t[1] = a.y * kLog2e; t[2] = a.z * kLog2e; t[3] = a.w * kLog2e;
-      t[4] = b.x * kLog2e; t[5] = b.y * kLog2e; t[6] = b.z * kLog2e; t[7] = b.w * kLog2e;
-    }
-    return;
-  }
-  size_t ie[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ie[e] = j0 + e < Lk ? idx + e : idx - j0;  // key 0 of the row: in bounds
-  if (md.kind == 1) {
-    const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
-    unsigned char v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = m8[ie[e]];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = (j0 + e < Lk && v[e] != 0) ? 0.f : -INFINITY;
   } else {
-    const float* m32 = static_cast<const float*>(md.mask);
-    float v[8];
+    if (vec) {
+      if constexpr (KIND == 1) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + idx);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = m32[ie[e]];
+        for (int e = 0; e < 8; ++e) t[e] = (((e < 4 ? u.x : u.y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx + 4);
+        t[0] = a.x * kLog2e; t[1] = a.y * kLog2e; t[2] = a.z * kLog2e; t[3] = a.w * kLog2e;
+        t[4] = b.x * kLog2e; t[5] = b.y * kLog2e; t[6] = b.z * kLog2e; t[7] = b.w * kLog2e;
+      }
+      return;
+    }
+    size_t ie[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? v[e] * kLog2e : -INFINITY;
+    for (int e = 0; e < 8; ++e) ie[e] = j0 + e < Lk ? idx + e : idx - j0;  // key 0 of the row: in bounds
+    if constexpr (KIND == 1) {
+      const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
+      unsigned char v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = m8[ie[e]];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = (j0 + e < Lk && v[e] != 0) ? 0.f : -INFINITY;
+    } else {
+      const float* m32 = static_cast<const float*>(md.mask);
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = m32[ie[e]];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? v[e] * kLog2e : -INFINITY;
+    }
   }
+}
+
+// The same with the kind read from md (a wave-uniform branch).
+__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
+                                            float (&t)[8]) {
+  if (md.kind == 0)
+    mask_terms8_kind<0>(md, idx, j0, Lk, vec, t);
+  else if (md.kind == 1)
+    mask_terms8_kind<1>(md, idx, j0, Lk, vec, t);
+  else
+    mask_terms8_kind<2>(md, idx, j0, Lk, vec, t);
 }
 
 }  // namespace attn

@@ -30,9 +30,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, PhiloxKey key) {
       k0 += W0;
       k1 += W1;
     }
-    const unsigned hi0 = __umulhi(M0, x.x), lo0 = M0 * x.x;
-    const unsigned hi1 = __umulhi(M1, x.z), lo1 = M1 * x.z;
-    x = make_uint4(hi1 ^ x.y ^ k0, lo1, hi0 ^ x.w ^ k1, lo0);
+    // Full 64-bit products: one v_mad_u64_u32 each instead of a
+    // v_mul_hi_u32 / v_mul_lo_u32 pair.
+    const uint64_t p0 = (uint64_t)M0 * x.x;
+    const uint64_t p1 = (uint64_t)M1 * x.z;
+    x = make_uint4((unsigned)(p1 >> 32) ^ x.y ^ k0, (unsigned)p1, (unsigned)(p0 >> 32) ^ x.w ^ k1, (unsigned)p0);
   }
   return x;
 }

@@ -39,7 +39,9 @@ using namespace st;
 constexpr int NT = 256;
 constexpr int BW = 128;  // queries per workgroup
 
-template <bool BF16, int D, bool CAUSAL>
+// KIND: mask kind (0 none, 1 boolean, 2 additive); DROP: dropout on.  Each
+// variant carries only its own per-element work.
+template <bool BF16, int D, bool CAUSAL, int KIND, bool DROP>
 __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDropout md, float c) {
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)qi * D + 16 * t + 8 * h);
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
-  const size_t mrow = md.kind != 0 && qi < Lq ? mask_slab(md, bh, Lq, Lk) + (size_t)qi * Lk : 0;
+  const size_t mrow = KIND != 0 && qi < Lq ? mask_slab(md, bh, Lq, Lk) + (size_t)qi * Lk : 0;
   const PhiloxKey pk{md.k0, md.k1};
 
   const int prow = perm_row(n);
@@ -116,12 +118,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     const char* Vs = stage + T::BYTES;
     // Mask terms of the tile's 32 keys, loaded before the score products so
     // that the loads overlap them.
-    const bool vec = Lk % 8 == 0 && kv0 + BQ <= Lk;  // whole, aligned mask rows for the tile
+    const bool whole = kv0 + BQ <= Lk;        // no key of the tile at or past Lk
+    const bool vec = Lk % 8 == 0 && whole;     // whole, aligned mask rows for the tile
     float t8[4][8];
+    if constexpr (KIND != 0) {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
-      mask_terms8(md, mrow + key0, key0, Lk, vec, t8[grp]);
+      for (int grp = 0; grp < 4; ++grp) {
+        const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
+        mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, vec, t8[grp]);
+      }
     }
     f32x16 s[2];
 #pragma unroll
@@ -132,22 +137,43 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         s[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s[b]);
     }
     // Register r of block b holds key kv0 + 32 b + 16 (r / 8) + 8 h + r % 8.
-    float mx = -INFINITY;
     unsigned keep[4] = {0xffu, 0xffu, 0xffu, 0xffu};
+    if constexpr (DROP) {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int b = grp >> 1, half = grp & 1;
-      const int key0 = kv0 + 32 * b + 16 * half + 8 * h;
-      if (md.dropout) keep[grp] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
+      for (int grp = 0; grp < 4; ++grp)
+        keep[grp] = dropout_keep8(pk, kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h, qi, bh, md.offset, md.thr);
+    }
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int r = 8 * half + e;
-        float x = __builtin_fmaf(s[b][r], c, t8[grp][e]);
-        if (CAUSAL && key0 + e > qi + off) x = -INFINITY;
-        s[b][r] = x;
-        mx = fmaxf(mx, x);
+        const int b = grp >> 1, r = 8 * (grp & 1) + e;
+        if constexpr (KIND != 0)
+          s[b][r] = __builtin_fmaf(s[b][r], c, t8[grp][e]);
+        else
+          s[b][r] *= c;
       }
+    // Keys past Lk (without a mask: only in the last tile) and, in tiles
+    // that cross the wave's first diagonal, keys past the query's diagonal.
+    if (KIND == 0 && !whole) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h + e >= Lk) s[grp >> 1][8 * (grp & 1) + e] = -INFINITY;
     }
+    if (CAUSAL && kv0 + BQ - 1 > wq0 + off) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h + e > qi + off) s[grp >> 1][8 * (grp & 1) + e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
     mx = halves_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -162,7 +188,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
       for (int e = 0; e < 8; ++e) {
         const float p = __builtin_amdgcn_exp2f(s[b][8 * half + e] - m_use);
         psum += p;
-        pb[grp][e] = (short)round16<BF16>(((keep[grp] >> e) & 1u) ? p : 0.f);
+        pb[grp][e] = (short)round16<BF16>(!DROP || ((keep[grp] >> e) & 1u) ? p : 0.f);
       }
     }
     // The correction exp(d_old - d_new) is 1 unless a row's maximum moved
@@ -204,7 +230,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   // Register r of block db holds column 32 db + 8 (r / 4) + 4 h + r % 4 of
   // the lane's query.
   const float l_tot = halves_sum(l_run);
-  const float inv = l_tot > 0.f ? (md.dropout ? md.rp : 1.f) / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROP ? md.rp : 1.f) / l_tot : 0.f;
   if (qi < Lq) {
     unsigned short* Og = static_cast<unsigned short*>(a.o) + ((size_t)bh * Lq + qi) * D;
 #pragma unroll
@@ -221,12 +247,24 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   }
 }
 
-template <bool BF16, int D, bool CAUSAL>
-hipError_t launch(const PrefillArgs& a, const MaskDropout& md, hipStream_t s) {
+template <bool BF16, int D, bool CAUSAL, int KIND, bool DROP>
+hipError_t launch_kd(const PrefillArgs& a, const MaskDropout& md, hipStream_t s) {
   const int nqb = (a.Lq + BW - 1) / BW;
   const float c = a.neg ? -a.c : a.c;
-  prefill_ex_kernel<BF16, D, CAUSAL><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md, c);
+  prefill_ex_kernel<BF16, D, CAUSAL, KIND, DROP><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md, c);
   return hipGetLastError();
+}
+
+// Neither mask nor dropout takes the dropout variant with p = 0 (threshold
+// 0 keeps every weight, 1 / (1 - p) = 1): correct, only slower; the entry
+// point sends that case to the plain kernel.
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch(const PrefillArgs& a, const MaskDropout& md, hipStream_t s) {
+  if (md.kind == 1)
+    return md.dropout ? launch_kd<BF16, D, CAUSAL, 1, true>(a, md, s) : launch_kd<BF16, D, CAUSAL, 1, false>(a, md, s);
+  if (md.kind == 2)
+    return md.dropout ? launch_kd<BF16, D, CAUSAL, 2, true>(a, md, s) : launch_kd<BF16, D, CAUSAL, 2, false>(a, md, s);
+  return launch_kd<BF16, D, CAUSAL, 0, true>(a, md, s);
 }
 
 template <bool BF16>
