@@ -56,7 +56,7 @@ constexpr int kStatFloats = 2 * BQ;  // per stats tile: lse2[64], then Dv[64]
 // into the following 512 B (a whole instruction, never read).
 __device__ __forceinline__ void dma_stats(const float* src, char* dst, int lane) {
   const unsigned off = 16u * (unsigned)(lane & 31);
-  dma_run<1>(reinterpret_cast<const char*>(src), &off, lds_addr(dst));
+  dma_run<1>(uniform_ptr(reinterpret_cast<const char*>(src)), &off, lds_addr(dst));
 }
 
 template <bool BF16>
@@ -209,10 +209,12 @@ __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, 
     __builtin_amdgcn_sched_barrier(0);
   });
 }
-// EX: a general mask and / or dropout (md) apply; the slot-scheduled fast
-// path is then off and every tile goes block by block.
-template <bool BF16, int D, bool CAUSAL, bool EX>
+// KIND (mask kind: 0 none, 1 boolean, 2 additive) and DROP (dropout): with
+// either, the slot-scheduled fast path is off and every tile goes block by
+// block; each variant carries only its own per-element work.
+template <bool BF16, int D, bool CAUSAL, int KIND, bool DROP>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout md) {
+  constexpr bool EX = KIND != 0 || DROP;
   using T = SwzTile<D>;
   constexpr int KS = D / 16;  // k-steps of a product over D
   constexpr int DB = D / 32;  // 32-column blocks of D
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       ta[db][hi] = row * T::PITCH + 16 * (chunk ^ T::swz(row)) + 8 * (li & 1);
     }
 
-  const size_t mslab = EX && md.kind != 0 ? mask_slab(md, bh, Lq, Lk) : 0;
+  const size_t mslab = KIND != 0 ? mask_slab(md, bh, Lq, Lk) : 0;
   const PhiloxKey pk{md.k0, md.k1};
 
   f32x16 dk[DB], dv[DB];
@@ -304,11 +306,91 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
     const char* Qs = stage;
     const char* dOs = stage + T::BYTES;
     const float* st = reinterpret_cast<const float*>(stage + 2 * T::BYTES);
+    // Mask terms and dropout keep bits do not depend on the products: they
+    // come first so that their loads and VALU work overlap the MFMAs.
+    // Mask terms (base 2) of the 16 elements: branch-free loads (elements
+    // outside [0, Lq) x [0, Lk) read element (0, 0) of the slab and get 0).
+    float mt[16];
+    if constexpr (EX) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt[r] = 0.f;
+    }
+    if constexpr (KIND != 0) {
+      size_t idx[16];
+      bool in[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+        in[r] = qi < Lq && key < Lk;
+        idx[r] = mslab + (in[r] ? (size_t)qi * Lk + key : 0);
+      }
+      if constexpr (KIND == 1) {
+        const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
+        unsigned char v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = m8[idx[r]];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt[r] = (in[r] && v[r] == 0) ? -INFINITY : 0.f;
+      } else {
+        const float* m32 = static_cast<const float*>(md.mask);
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = m32[idx[r]];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt[r] = in[r] ? v[r] * kLog2e : 0.f;
+      }
+    }
+    // Dropout keep bits of the 16 elements (bit r).  Element r needs word
+    // (key mod 4) of the Philox block of (key / 4, query of r); the 4 lanes of
+    // a quad hold keys 4m .. 4m+3 of one half-wave and need the same 16
+    // blocks.  Lane u of the quad computes the blocks of r = 4 t + u, and the
+    // quad exchanges words with DPP quad permutations: in rotation k, lane v
+    // offers word (v + k) mod 4 of its block and lane u takes it from lane
+    // (u - k) mod 4 -- word u of the block of r = 4 t + ((u - k) mod 4).
+    unsigned kbits = 0xFFFFu;
+    if constexpr (DROP) {
+      kbits = 0u;
+      const int u = n & 3;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * t + u;
+        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
+        const uint4 wd = philox4x32_10(make_uint4((unsigned)key >> 2, (unsigned)qi, (unsigned)bh, md.offset), pk);
+        const unsigned wv[4] = {wd.x, wd.y, wd.z, wd.w};
+        static_for<4>([&](auto K) __attribute__((always_inline)) {
+          constexpr int k = decltype(K)::value;
+          // Word (u + k) mod 4 by bit masks: a lane-dependent ternary chain
+          // here becomes divergent branches.
+          const unsigned sel = (unsigned)(u + k);
+          const unsigned m0 = 0u - (sel & 1u), m1 = 0u - ((sel >> 1) & 1u);
+          const unsigned a01 = (wv[1] & m0) | (wv[0] & ~m0);
+          const unsigned a23 = (wv[3] & m0) | (wv[2] & ~m0);
+          const unsigned offer = (a23 & m1) | (a01 & ~m1);
+          // quad_perm control: lane u reads lane (u - k) mod 4
+          constexpr int kPerm = ((0 - k) & 3) | (((1 - k) & 3) << 2) | (((2 - k) & 3) << 4) | (((3 - k) & 3) << 6);
+          unsigned got = offer;
+          if constexpr (k != 0) got = (unsigned)__builtin_amdgcn_mov_dpp((int)offer, kPerm, 0xF, 0xF, false);
+          const int rr = 4 * t + ((u - k) & 3);
+          kbits |= (got >= md.thr ? 1u : 0u) << rr;
+        });
+      }
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       s = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Qs + 32 * b * T::PITCH + ra[t]), kreg[t], s);
       dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(dOs + 32 * b * T::PITCH + ra[t]), vreg[t], dp);
+    }
+    if constexpr (DROP) {
+      // Interleave the Philox rounds with the 16 products: after the first
+      // operand reads, each MFMA is followed by one operand read and ~16
+      // VALU instructions, which issue while the MFMA runs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      static_for<2 * KS>([&](auto) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      });
     }
     // Register r holds query qb + 16 (r / 8) + 8 h + r % 8 of key kw0 + n.
     float l2[16], dd[16];
@@ -321,69 +403,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       *reinterpret_cast<float4*>(dd + 8 * hh + 4) = *reinterpret_cast<const float4*>(st + BQ + base + 4);
     }
     const bool masked = CAUSAL && qb + off < kw0 + 31;
-    // Mask terms (base 2) of the 16 elements: branch-free loads (elements
-    // outside [0, Lq) x [0, Lk) read element (0, 0) of the slab and get 0).
-    float mt[16];
+    if constexpr (!EX) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt[r] = 0.f;
-    if constexpr (EX) {
-      if (md.kind != 0) {
-        size_t idx[16];
-        bool in[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-          in[r] = qi < Lq && key < Lk;
-          idx[r] = mslab + (in[r] ? (size_t)qi * Lk + key : 0);
-        }
-        if (md.kind == 1) {
-          const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
-          unsigned char v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = m8[idx[r]];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mt[r] = (in[r] && v[r] == 0) ? -INFINITY : 0.f;
-        } else {
-          const float* m32 = static_cast<const float*>(md.mask);
-          float v[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = m32[idx[r]];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mt[r] = in[r] ? v[r] * kLog2e : 0.f;
-        }
-      }
-    }
-    // Dropout keep bits of the 16 elements (bit r).  Element r needs word
-    // (key mod 4) of the Philox block of (key / 4, query of r); the 4 lanes of
-    // a quad hold keys 4m .. 4m+3 of one half-wave and need the same 16
-    // blocks.  Lane u of the quad computes the blocks of r = 4 t + u, and the
-    // quad exchanges words with DPP quad permutations: in rotation k, lane v
-    // offers word (v + k) mod 4 of its block and lane u takes it from lane
-    // (u - k) mod 4 -- word u of the block of r = 4 t + ((u - k) mod 4).
-    unsigned kbits = 0xFFFFu;
-    if constexpr (EX) {
-      if (md.dropout) {
-        kbits = 0u;
-        const int u = n & 3;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * t + u;
-          const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-          const uint4 wd = philox4x32_10(make_uint4((unsigned)key >> 2, (unsigned)qi, (unsigned)bh, md.offset), pk);
-          const unsigned wv[4] = {wd.x, wd.y, wd.z, wd.w};
-          static_for<4>([&](auto K) __attribute__((always_inline)) {
-            constexpr int k = decltype(K)::value;
-            const int sel = (u + k) & 3;
-            const unsigned offer = sel == 0 ? wv[0] : sel == 1 ? wv[1] : sel == 2 ? wv[2] : wv[3];
-            // quad_perm control: lane u reads lane (u - k) mod 4
-            constexpr int kPerm = ((0 - k) & 3) | (((1 - k) & 3) << 2) | (((2 - k) & 3) << 4) | (((3 - k) & 3) << 6);
-            unsigned got = offer;
-            if constexpr (k != 0) got = (unsigned)__builtin_amdgcn_mov_dpp((int)offer, kPerm, 0xF, 0xF, false);
-            const int rr = 4 * t + ((u - k) & 3);
-            kbits |= (got >= md.thr ? 1u : 0u) << rr;
-          });
-        }
-      }
+      for (int r = 0; r < 16; ++r) mt[r] = 0.f;
     }
     s16x8 pa[2], sa[2];
 #pragma unroll
@@ -394,8 +416,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       // Dropout: the value product sees the kept weights scaled by 1/(1-p),
       // and dP reaches the softmax through the same factors.
       float pv = p, dpk = dp[r];
-      if constexpr (EX) {
-        const float z = ((kbits >> r) & 1u) ? md.rp : 0.f;  // md.rp = 1 without dropout
+      if constexpr (DROP) {
+        const float z = ((kbits >> r) & 1u) ? md.rp : 0.f;
         pv = p * z;
         dpk = dpk * z;
       }
@@ -511,8 +533,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 128 queries, loop over 64-key tiles.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL, bool EX>
+template <bool BF16, int D, bool CAUSAL, int KIND, bool DROP>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md) {
+  constexpr bool EX = KIND != 0 || DROP;
   using T = SwzTile<D>;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -575,7 +598,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
   }
   // Row of the lane's query in the mask (row 0 of the slab for padded
   // queries: in bounds, never stored).
-  const size_t mrow = EX && md.kind != 0 ? mask_slab(md, bh, Lq, Lk) + (size_t)(qi < Lq ? qi : 0) * Lk : 0;
+  const size_t mrow = KIND != 0 ? mask_slab(md, bh, Lq, Lk) + (size_t)(qi < Lq ? qi : 0) * Lk : 0;
   const PhiloxKey pk{md.k0, md.k1};
 
   const int prow = perm_row(n);
@@ -603,14 +626,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     if (kb0 >= w_key_end) return;
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      s = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s);
-      dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp);
-    }
-    // Register r holds key kb0 + 16 (r / 8) + 8 h + r % 8 of query qi.
-    const bool masked = kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off);
+    // Mask terms and keep bits first: independent of the products, their
+    // loads and VALU work overlap the MFMAs.
     float mt[16];
     unsigned keep[2] = {0xffu, 0xffu};
 #pragma unroll
@@ -619,12 +636,20 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int key0 = kb0 + 16 * half + 8 * h;
-        if (md.kind != 0)
-          mask_terms8(md, mrow + key0, key0, Lk, Lk % 8 == 0 && kb0 + 32 <= Lk,
-                      *reinterpret_cast<float(*)[8]>(mt + 8 * half));
-        if (md.dropout) keep[half] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
+        if constexpr (KIND != 0)
+          mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, Lk % 8 == 0 && kb0 + 32 <= Lk,
+                                 *reinterpret_cast<float(*)[8]>(mt + 8 * half));
+        if constexpr (DROP) keep[half] = dropout_keep8(pk, key0, qi, bh, md.offset, md.thr);
       }
     }
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      s = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s);
+      dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp);
+    }
+    // Register r holds key kb0 + 16 (r / 8) + 8 h + r % 8 of query qi.
+    const bool masked = kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off);
     s16x8 sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -634,9 +659,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
         if (kj >= Lk || (CAUSAL && kj > qi + off)) p = 0.f;
       }
       float dpk = dp[r];
-      if constexpr (EX) {
-        if (md.dropout) dpk = ((keep[r >> 3] >> (r & 7)) & 1u) ? dpk * md.rp : 0.f;
-      }
+      if constexpr (DROP) dpk = ((keep[r >> 3] >> (r & 7)) & 1u) ? dpk * md.rp : 0.f;
       sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dpk - dd));
     }
     // dQ += dS K over the block's 32 keys (2 k-steps).
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
   }
 }
 
-template <int DT, int D, bool CAUSAL, bool EX>
+template <int DT, int D, bool CAUSAL, int KIND, bool DROP>
 hipError_t launch_typed(const BwdArgs& a, const MaskDropout& md, hipStream_t s) {
   const int nqt = (a.Lq + BQ - 1) / BQ;
   bwd_stats_kernel<DT, D><<<dim3(a.BH * nqt), dim3(NT), 0, s>>>(a);
@@ -690,10 +713,10 @@ hipError_t launch_typed(const BwdArgs& a, const MaskDropout& md, hipStream_t s) 
   if (e != hipSuccess) return e;
   const int nkb = (a.Lk + BW - 1) / BW;
   const int nqb = (a.Lq + BW - 1) / BW;
-  bwd_dkdv_kernel<DT == 2, D, CAUSAL, EX><<<dim3(a.BH * nkb), dim3(NT), 0, s>>>(a, md);
+  bwd_dkdv_kernel<DT == 2, D, CAUSAL, KIND, DROP><<<dim3(a.BH * nkb), dim3(NT), 0, s>>>(a, md);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_dq_kernel<DT == 2, D, CAUSAL, EX><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md);
+  bwd_dq_kernel<DT == 2, D, CAUSAL, KIND, DROP><<<dim3(a.BH * nqb), dim3(NT), 0, s>>>(a, md);
   return hipGetLastError();
 }
 
@@ -703,19 +726,26 @@ size_t bwd_workspace_bytes(int BH, int Lq) {
   return (size_t)BH * ((Lq + BQ - 1) / BQ) * kStatFloats * sizeof(float);
 }
 
-template <int DT, bool EX>
-hipError_t launch_ex(int D, bool causal, const BwdArgs& a, const MaskDropout& md, hipStream_t s) {
+template <int DT, int KIND, bool DROP>
+hipError_t launch_kd(int D, bool causal, const BwdArgs& a, const MaskDropout& md, hipStream_t s) {
   if (D == 128)
-    return causal ? launch_typed<DT, 128, true, EX>(a, md, s) : launch_typed<DT, 128, false, EX>(a, md, s);
-  return causal ? launch_typed<DT, 64, true, EX>(a, md, s) : launch_typed<DT, 64, false, EX>(a, md, s);
+    return causal ? launch_typed<DT, 128, true, KIND, DROP>(a, md, s)
+                  : launch_typed<DT, 128, false, KIND, DROP>(a, md, s);
+  return causal ? launch_typed<DT, 64, true, KIND, DROP>(a, md, s) : launch_typed<DT, 64, false, KIND, DROP>(a, md, s);
+}
+
+template <int DT>
+hipError_t launch_dt(int D, bool causal, const BwdArgs& a, const MaskDropout* md, hipStream_t s) {
+  if (md == nullptr || (md->kind == 0 && !md->dropout)) return launch_kd<DT, 0, false>(D, causal, a, MaskDropout{}, s);
+  if (md->kind == 1)
+    return md->dropout ? launch_kd<DT, 1, true>(D, causal, a, *md, s) : launch_kd<DT, 1, false>(D, causal, a, *md, s);
+  if (md->kind == 2)
+    return md->dropout ? launch_kd<DT, 2, true>(D, causal, a, *md, s) : launch_kd<DT, 2, false>(D, causal, a, *md, s);
+  return launch_kd<DT, 0, true>(D, causal, a, *md, s);
 }
 
 hipError_t launch_bwd(int dtype, int D, bool causal, const BwdArgs& a, hipStream_t s, const MaskDropout* md) {
-  const bool ex = md != nullptr && (md->kind != 0 || md->dropout);
-  MaskDropout none{};
-  const MaskDropout& m = ex ? *md : none;
-  if (dtype == 2) return ex ? launch_ex<2, true>(D, causal, a, m, s) : launch_ex<2, false>(D, causal, a, m, s);
-  return ex ? launch_ex<1, true>(D, causal, a, m, s) : launch_ex<1, false>(D, causal, a, m, s);
+  return dtype == 2 ? launch_dt<2>(D, causal, a, md, s) : launch_dt<1>(D, causal, a, md, s);
 }
 
 }  // namespace attn

@@ -40,12 +40,23 @@ struct SwzTile {
   }
 };
 
+// A wave-uniform pointer, made visibly uniform (an SGPR pair) for the DMA's
+// scalar base operand: some kernels' uniformity analysis leaves such a
+// pointer in VGPRs.  No code when it already is in SGPRs.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
 // DMA of one 64-row tile (row 0 at `src`) into swizzled LDS.  Rows at or
 // past rows_left (>= 1) fetch row rows_left - 1 instead (in bounds; their
 // results are discarded or zero-weighted).  `src` must be wave-uniform.
 template <int D>
-__device__ __forceinline__ void dma_swz_tile(const char* src, char* dst, int w, int lane, int rows_left) {
+__device__ __forceinline__ void dma_swz_tile(const char* src_any, char* dst, int w, int lane, int rows_left) {
   using T = SwzTile<D>;
+  const char* src = uniform_ptr(src_any);
 #pragma unroll
   for (int i = 0; i < T::PER_WAVE; ++i) {
     const int inst = w * T::PER_WAVE + i;

@@ -187,6 +187,8 @@ def cmd_ex(args):
     cases = [("plain", None, 0.0), ("bool mask", bmask, 0.0), ("additive mask", amask, 0.0),
              ("dropout 0.1", None, 0.1), ("bool mask + dropout 0.1", bmask, 0.1)]
     for label, mask, p in cases:
+        if args.case and label != args.case:
+            continue
         if label == "plain":
             fwd = lambda: binding.attn_fwd(q, k, v, causal=True, scale=wl.scale)
         else:
@@ -209,6 +211,7 @@ def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("cmd", choices=["kernels", "copy", "sweep", "sweep_ext", "ex"])
     p.add_argument("--reps", type=int, default=5)
+    p.add_argument("--case", default="", help="ex: run only the case with this label")
     args = p.parse_args(argv)
     if not torch.cuda.is_available():
         print("needs a GPU", file=sys.stderr)
