@@ -231,6 +231,20 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 int attn_decode_auto_splits(int B, int H, int Lk, int D);
 
 /*
+ * attn_prefill_split_plan - how attn_fwd cuts the keys of a prefill that
+ * runs on the two-group kernel (fp16 / bf16, D = 128, scale != 0) on a
+ * device with num_cus compute units.  Pure host arithmetic, launches
+ * nothing.  ranges[ceil(Lq / 256)] (caller-owned) receives the number of key
+ * ranges of each 256-row query tile, all 1 when the shape is not split;
+ * *items receives the work items per (batch, head), the sum of ranges.
+ * forced: as the ATTN_PREFILL_SPLITS environment variable (0 = automatic).
+ * Returns ATTN_OK, ATTN_ERR_DIM for a non-positive size, num_cus or a
+ * negative forced, ATTN_ERR_NULL for a null pointer.
+ */
+int attn_prefill_split_plan(int B, int H, int Lq, int Lk, int causal, int num_cus, int forced,
+                            int* ranges, int* items);
+
+/*
  * attn_strerror - static description of a status code.  For ATTN_ERR_HIP
  * the text of the last HIP error seen by the calling host thread is
  * appended; the returned pointer stays valid until that thread's next

@@ -23,7 +23,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_bwd", "attn_fwd_ex", "attn_bwd_ex",
-            "attn_decode_auto_splits", "attn_strerror")
+            "attn_decode_auto_splits", "attn_prefill_split_plan", "attn_strerror")
 ATTN_MASK_NONE, ATTN_MASK_BOOL, ATTN_MASK_ADD = 0, 1, 2
 
 _lock = threading.Lock()
@@ -69,6 +69,9 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd_ex.restype = i
         lib.attn_decode_auto_splits.argtypes = [i, i, i, i]
         lib.attn_decode_auto_splits.restype = i
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.attn_prefill_split_plan.argtypes = [i, i, i, i, i, i, i, ip, ip]
+        lib.attn_prefill_split_plan.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -77,6 +80,18 @@ def load() -> ctypes.CDLL:
 
 def attn_strerror(status: int) -> str:
     return load().attn_strerror(int(status)).decode()
+
+
+def attn_prefill_split_plan(B: int, H: int, Lq: int, Lk: int, causal: bool, num_cus: int, forced: int = 0):
+    """Key ranges per 256-row query tile that attn_fwd uses for this prefill
+    on a device with num_cus compute units, and the work items per
+    (batch, head).  Host arithmetic only."""
+    nqt = (max(Lq, 1) + 255) // 256
+    ranges = (ctypes.c_int * nqt)()
+    items = ctypes.c_int()
+    _check(load().attn_prefill_split_plan(int(B), int(H), int(Lq), int(Lk), int(bool(causal)), int(num_cus),
+                                          int(forced), ranges, ctypes.byref(items)))
+    return list(ranges), items.value
 
 
 def _check(status: int) -> None:

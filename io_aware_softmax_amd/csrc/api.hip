@@ -67,17 +67,17 @@ int prefill_variant() {
   return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
 }
 
-// Key-range count of the two-group prefill: ATTN_PREFILL_SPLITS=n forces
-// n (1 = never split; capped so that no range is empty), else the library
-// chooses from the shape and the device's compute-unit count.
-hipError_t prefill_splits(int BH, int Lq, int Lk, bool causal, int* out) {
+// Key ranges of the two-group prefill: ATTN_PREFILL_SPLITS=n forces n per
+// query tile (1 = never split; capped so that no range is empty), else the
+// library plans them from the shape and the device's compute-unit count.
+hipError_t prefill_split_plan(int BH, int Lq, int Lk, bool causal, attn::PrefillSplitPlan* plan, bool* split) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const char* env = std::getenv("ATTN_PREFILL_SPLITS");
   const int forced = (env != nullptr && *env != '\0') ? std::max(1, std::atoi(env)) : 0;
-  *out = attn::prefill_pp_auto_splits(BH, Lq, Lk, causal, cus, forced);
+  *split = attn::prefill_pp_plan_splits(BH, Lq, Lk, causal, cus, forced, plan);
   return hipSuccess;
 }
 
@@ -248,18 +248,19 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
   } else if (D == 128 && a.c > 0.f && prefill_variant() != 1) {
     // Shapes with fewer query tiles than the part has compute units (one
     // head, short chunks) cut each tile's keys into ranges, merged after.
-    int n_split = 1;
-    e = prefill_splits(a.BH, Lq, Lk, causal != 0, &n_split);
+    attn::PrefillSplitPlan plan;
+    bool split = false;
+    e = prefill_split_plan(a.BH, Lq, Lk, causal != 0, &plan, &split);
     if (e != hipSuccess) return hip_fail(e);
-    if (n_split > 1) {
+    if (split) {
       const size_t rows = size_t(a.BH) * Lq;
-      const size_t bytes = size_t(n_split) * rows * (size_t(D) + 1) * sizeof(float);
+      const size_t ranges = size_t(plan.max_ranges);
+      const size_t bytes = ranges * rows * (size_t(D) + 1) * sizeof(float);
       void* ws = nullptr;
       e = hipMallocAsync(&ws, bytes, s);
       if (e != hipSuccess) return hip_fail(e);
       float* part_o = static_cast<float*>(ws);
-      e = attn::launch_prefill_pp_split(dtype, causal != 0, a, n_split, part_o, part_o + size_t(n_split) * rows * D,
-                                        s);
+      e = attn::launch_prefill_pp_split(dtype, causal != 0, a, plan, part_o, part_o + ranges * rows * D, s);
       const hipError_t ef = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = ef;
     } else {
@@ -362,6 +363,23 @@ ATTN_EXPORT int attn_decode_auto_splits(int B, int H, int Lk, int D) {
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED_D;
   if (int64_t(B) * H > INT32_MAX) return ATTN_ERR_DIM;
   return auto_splits(int64_t(B) * H, Lk);
+}
+
+ATTN_EXPORT int attn_prefill_split_plan(int B, int H, int Lq, int Lk, int causal, int num_cus, int forced,
+                                        int* ranges, int* items) {
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || num_cus <= 0 || forced < 0) return ATTN_ERR_DIM;
+  if (ranges == nullptr || items == nullptr) return ATTN_ERR_NULL;
+  if (int64_t(B) * H > INT32_MAX) return ATTN_ERR_DIM;
+  const int nqt = (Lq + 255) / 256;
+  attn::PrefillSplitPlan plan;
+  if (attn::prefill_pp_plan_splits(B * H, Lq, Lk, causal != 0, num_cus, forced, &plan)) {
+    for (int qt = 0; qt < nqt; ++qt) ranges[qt] = plan.ranges[qt];
+    *items = plan.items;
+  } else {
+    for (int qt = 0; qt < nqt; ++qt) ranges[qt] = 1;
+    *items = nqt;
+  }
+  return ATTN_OK;
 }
 
 ATTN_EXPORT const char* attn_strerror(int status) {

@@ -82,14 +82,30 @@ hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out)
 hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Two-group (ping-pong) variant of the 16-bit prefill for D = 128.
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
-// The same with every query tile's keys cut into n_split ranges (partials in
-// part_o [n_split, BH, Lq, 128] and part_l [n_split, BH, Lq] fp32), then merged.
-hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, int n_split, float* part_o,
-                                   float* part_l, hipStream_t s);
-// Key-range count for launch_prefill_pp_split on a part with `cus` compute
-// units (1: do not split): only shapes with fewer than cus / 2 query tiles.
-// forced > 0 asks for that count, capped so that no range is empty.
-int prefill_pp_auto_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced);
+// Key ranges of a split prefill: query tile qt (256 rows) of every
+// (batch, head) has ranges[qt] contiguous, balanced, non-empty ranges of its
+// 64-key tiles; item[t] = (qt << 5) | range lists the `items` ranges of one
+// (batch, head), heaviest tiles first.  Passed by value to the kernels.
+constexpr int kSplitMaxItems = 256;
+constexpr int kSplitMaxTiles = 128;
+constexpr int kSplitMaxRanges = 32;
+struct PrefillSplitPlan {
+  int items;       // ranges per (batch, head)
+  int max_ranges;  // largest ranges[qt]: the partial buffers' leading extent
+  unsigned short item[kSplitMaxItems];
+  unsigned char ranges[kSplitMaxTiles];
+};
+// The same with the keys of every query tile cut as `plan` says (partials in
+// part_o [max_ranges, BH, Lq, 128] and part_l [max_ranges, BH, Lq] fp32),
+// then merged.
+hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, const PrefillSplitPlan& plan,
+                                   float* part_o, float* part_l, hipStream_t s);
+// Plans the split on a part with `cus` compute units; false: do not split.
+// Automatic (forced == 0): only shapes with at most cus / 2 query tiles; the
+// ranges hold about R key tiles each, R the smallest value (>= 8) for which
+// one range per workgroup covers the shape.  forced > 0: that many ranges
+// for every tile, capped at 16 and so that no range is empty.
+bool prefill_pp_plan_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced, PrefillSplitPlan* plan);
 // The same algorithm with fp32 inputs on the fp32 MFMA.
 hipError_t launch_prefill_f32(int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Forward with a general mask and / or dropout (16-bit dtypes).

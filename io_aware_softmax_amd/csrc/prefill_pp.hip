@@ -129,16 +129,17 @@ __device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbas
   }
 }
 
-// SPLIT: every (batch*head, query tile) is cut into n_split contiguous key
-// ranges, each an item of its own; an item writes its rows' normalised
-// partial output and log-sum-exp (part_o, part_l) instead of O and LSE, and
-// prefill_split_combine merges them.
+// SPLIT: the keys of every (batch*head, query tile) are cut into the
+// contiguous ranges `plan` lists, each an item of its own; an item writes its
+// rows' normalised partial output and log-sum-exp (part_o, part_l) instead of
+// O and LSE, and prefill_split_combine merges them.  The unsplit kernel never
+// reads the last three arguments.
 template <bool BF16, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ O, float* __restrict__ LSE, int BH,
-    int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd, int n_split,
-    float* __restrict__ part_o, float* __restrict__ part_l) {
+    int Lq, int Lk, int nqt, float c, unsigned qsign, int slots_per_xcd, int items_per_xcd,
+    float* __restrict__ part_o, float* __restrict__ part_l, const PrefillSplitPlan plan) {
   using T = Tile<D>;
   using LY = Layout<D>;
   using KP = DmaPlan<T::KINST, kRun, kDmaWaves>;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // tiles with light ones); a workgroup with several items runs them one
   // after the other and loads the next item's first tiles and Q while it
   // writes the current output.
-  const int total = BH * nqt * (SPLIT ? n_split : 1);
+  const int total = BH * (SPLIT ? plan.items : nqt);
   const int wg = blockIdx.x;
   const int xcd = wg % 8, slot = wg / 8;
   const int range_lo = xcd * items_per_xcd;
@@ -186,13 +187,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   const char* Vb = nullptr;
   s16x8 qreg[T::KSTEPS];
   auto setup = [&](int logical) __attribute__((always_inline)) {
-    int tile_item = logical;
+    int qt, n_ranges = 1;
     if constexpr (SPLIT) {
-      sp_s = logical % n_split;
-      tile_item = logical / n_split;
+      bh = logical / plan.items;
+      const unsigned e = plan.item[logical % plan.items];
+      qt = (int)(e >> 5);
+      sp_s = (int)(e & 31u);
+      n_ranges = plan.ranges[qt];
+    } else {
+      bh = logical / nqt;
+      qt = CAUSAL ? nqt - 1 - logical % nqt : logical % nqt;
     }
-    bh = tile_item / nqt;
-    const int qt = CAUSAL ? nqt - 1 - tile_item % nqt : tile_item % nqt;
     const int q0 = qt * kRows;
     Kb = reinterpret_cast<const char*>(K + (size_t)bh * Lk * D);
     Vb = reinterpret_cast<const char*>(V + (size_t)bh * Lk * D);
@@ -213,10 +218,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     j_mask = __builtin_amdgcn_readfirstlane(jm);
     if constexpr (SPLIT) {
       // Key tiles [jl, jh) of the query tile's [0, nkv), balanced so that no
-      // range is empty (the launch keeps n_split <= every tile's nkv); the
+      // range is empty (the plan keeps a tile's range count <= its nkv); the
       // counts below become local to that range.
-      const int jl = sp_s * nkv / n_split;
-      const int jh = (sp_s + 1) * nkv / n_split;
+      const int jl = sp_s * nkv / n_ranges;
+      const int jh = (sp_s + 1) * nkv / n_ranges;
       jl_s = __builtin_amdgcn_readfirstlane(jl);
       nkv = __builtin_amdgcn_readfirstlane(jh - jl);
       w_nkv = __builtin_amdgcn_readfirstlane(max(0, min(w_nkv - jl, nkv)));
@@ -571,10 +576,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
 }
 
 template <bool BF16, bool CAUSAL, bool SPLIT>
-hipError_t launch(const PrefillArgs& a, hipStream_t s, int n_split, float* part_o, float* part_l) {
+hipError_t launch(const PrefillArgs& a, hipStream_t s, const PrefillSplitPlan& plan, float* part_o, float* part_l) {
   const int nqt = (a.Lq + kRows - 1) / kRows;
   const unsigned qsign = a.neg ? 0x80008000u : 0u;
-  const int total = a.BH * nqt * (SPLIT ? n_split : 1);
+  const int total = a.BH * (SPLIT ? plan.items : nqt);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -600,12 +605,13 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s, int n_split, float* part_
   hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
                      static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse, a.BH, a.Lq,
-                     a.Lk, nqt, a.c, qsign, slots, per, n_split, part_o, part_l);
+                     a.Lk, nqt, a.c, qsign, slots, per, part_o, part_l, plan);
   return hipGetLastError();
 }
 
 // Merge of the key ranges of a split prefill, one row of D = 128 per 128
-// threads: with lse_p the ranges' log-sum-exps and m = max_p lse_p,
+// threads; the row's query tile has plan.ranges[qt] ranges.  With lse_p the
+// ranges' log-sum-exps and m = max_p lse_p,
 // O = sum_p exp(lse_p - m) O_p / sum_p exp(lse_p - m) and
 // LSE = m + ln sum_p exp(lse_p - m) -- the guide's output correction with a
 // key range as the chunk (ranges without a key, lse_p = -inf, drop out).
@@ -613,10 +619,11 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void prefill_split_combine(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_l,
                                                              unsigned short* __restrict__ O, float* __restrict__ LSE,
-                                                             int rows, int n_split) {
+                                                             int rows, int Lq, const PrefillSplitPlan plan) {
   const int row = blockIdx.x * 2 + (threadIdx.x >> 7);  // (b h) * Lq + q
   const int d = threadIdx.x & 127;
   if (row >= rows) return;
+  const int n_split = plan.ranges[(row % Lq) / kRows];
   float m = -INFINITY;
   for (int p = 0; p < n_split; ++p) m = fmaxf(m, part_l[(size_t)p * rows + row]);
   float acc = 0.f, wsum = 0.f;
@@ -635,53 +642,80 @@ __global__ __launch_bounds__(256) void prefill_split_combine(const float* __rest
 }  // namespace
 
 hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s) {
+  static const PrefillSplitPlan none{};  // not read by the unsplit kernel
   if (dtype == 2)
-    return causal ? launch<true, true, false>(a, s, 1, nullptr, nullptr)
-                  : launch<true, false, false>(a, s, 1, nullptr, nullptr);
-  return causal ? launch<false, true, false>(a, s, 1, nullptr, nullptr)
-                : launch<false, false, false>(a, s, 1, nullptr, nullptr);
+    return causal ? launch<true, true, false>(a, s, none, nullptr, nullptr)
+                  : launch<true, false, false>(a, s, none, nullptr, nullptr);
+  return causal ? launch<false, true, false>(a, s, none, nullptr, nullptr)
+                : launch<false, false, false>(a, s, none, nullptr, nullptr);
 }
 
-hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, int n_split, float* part_o,
-                                   float* part_l, hipStream_t s) {
+hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, const PrefillSplitPlan& plan,
+                                   float* part_o, float* part_l, hipStream_t s) {
   hipError_t e;
   if (dtype == 2)
-    e = causal ? launch<true, true, true>(a, s, n_split, part_o, part_l)
-               : launch<true, false, true>(a, s, n_split, part_o, part_l);
+    e = causal ? launch<true, true, true>(a, s, plan, part_o, part_l)
+               : launch<true, false, true>(a, s, plan, part_o, part_l);
   else
-    e = causal ? launch<false, true, true>(a, s, n_split, part_o, part_l)
-               : launch<false, false, true>(a, s, n_split, part_o, part_l);
+    e = causal ? launch<false, true, true>(a, s, plan, part_o, part_l)
+               : launch<false, false, true>(a, s, plan, part_o, part_l);
   if (e != hipSuccess) return e;
   const int rows = a.BH * a.Lq;
   if (dtype == 2)
     prefill_split_combine<true><<<dim3((rows + 1) / 2), dim3(256), 0, s>>>(
-        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, n_split);
+        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, a.Lq, plan);
   else
     prefill_split_combine<false><<<dim3((rows + 1) / 2), dim3(256), 0, s>>>(
-        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, n_split);
+        part_o, part_l, static_cast<unsigned short*>(a.o), a.lse, rows, a.Lq, plan);
   return hipGetLastError();
 }
 
-int prefill_pp_auto_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced) {
+bool prefill_pp_plan_splits(int BH, int Lq, int Lk, bool causal, int cus, int forced, PrefillSplitPlan* plan) {
   const int nqt = (Lq + kRows - 1) / kRows;
-  const long long items = (long long)BH * nqt;
-  // Key tiles of the smallest query tile (every range must be non-empty)
-  // and of the average one (ranges of at least 8 tiles).
+  if (nqt < 1 || nqt > kSplitMaxTiles) return false;
   const int off = Lk - Lq;
-  const int min_nkv = causal ? (min(Lk, min(kRows, Lq) + off) + BN - 1) / BN : (Lk + BN - 1) / BN;
-  if (forced > 0) return max(1, min(forced, min(min_nkv, 16)));
-  if (items * 2 > cus) return 1;
+  int nkv[kSplitMaxTiles];
   long long kv_sum = 0;
+  int min_nkv = 1 << 30;
   for (int qt = 0; qt < nqt; ++qt) {
     const int q_last = min((qt + 1) * kRows, Lq) - 1;
-    kv_sum += causal ? (min(Lk, q_last + off + 1) + BN - 1) / BN : (Lk + BN - 1) / BN;
+    nkv[qt] = causal ? (min(Lk, q_last + off + 1) + BN - 1) / BN : (Lk + BN - 1) / BN;
+    kv_sum += nkv[qt];
+    min_nkv = min(min_nkv, nkv[qt]);
   }
-  const long long avg_nkv = kv_sum / nqt;
-  long long sp = cus / items;
-  sp = min(sp, (long long)min_nkv);
-  sp = min(sp, avg_nkv / 8);
-  sp = min(sp, 16LL);
-  return sp >= 2 ? (int)sp : 1;
+  if (min_nkv < 1) return false;  // a tile without keys: the unsplit kernel handles it
+  int count[kSplitMaxTiles];
+  if (forced > 0) {
+    const int sp = min(forced, min(min_nkv, 16));
+    if (sp < 2 || (long long)nqt * sp > kSplitMaxItems) return false;
+    for (int qt = 0; qt < nqt; ++qt) count[qt] = sp;
+  } else {
+    if ((long long)BH * nqt * 2 > cus) return false;
+    // Range size R (key tiles): from an even share of the whole job per
+    // compute unit, grown until one range per workgroup covers the shape.
+    long long R = max(8LL, ((long long)BH * kv_sum + cus - 1) / cus);
+    for (;; ++R) {
+      long long items = 0;
+      for (int qt = 0; qt < nqt; ++qt) {
+        count[qt] = (int)min((long long)kSplitMaxRanges, (nkv[qt] + R - 1) / R);
+        items += count[qt];
+      }
+      if (items <= kSplitMaxItems && BH * items <= cus) break;
+    }
+    bool any = false;
+    for (int qt = 0; qt < nqt; ++qt) any = any || count[qt] > 1;
+    if (!any) return false;
+  }
+  int t = 0, mx = 1;
+  for (int i = 0; i < nqt; ++i) {
+    const int qt = causal ? nqt - 1 - i : i;  // heaviest tiles first
+    plan->ranges[qt] = (unsigned char)count[qt];
+    mx = max(mx, count[qt]);
+    for (int sp = 0; sp < count[qt]; ++sp) plan->item[t++] = (unsigned short)((qt << 5) | sp);
+  }
+  plan->items = t;
+  plan->max_ranges = mx;
+  return true;
 }
 
 }  // namespace attn
