@@ -91,14 +91,16 @@ typedef enum {
  * stream-ordered workspace of (D + 2) * 4 * B * H * splits bytes with
  * hipMallocAsync on `stream` and releases it on the same stream.
  *
- * A 16-bit prefill at D = 128 with fewer 256-row query tiles than half the
- * device's compute units (one head, a short chunk against a long cache)
- * cuts each query tile's keys into up to 16 ranges, computed in parallel
- * and merged with the guide's output correction, each range taken as one
- * chunk (as attn_decode_fwd below does for one query).  It
- * allocates (D + 1) * 4 * B * H * Lq * ranges bytes the same stream-ordered
- * way.  The environment variable ATTN_PREFILL_SPLITS=n forces n ranges
- * (capped so that no range is empty; 1 never splits).
+ * A 16-bit prefill at D = 128 with at most half as many 256-row query
+ * tiles as the device has compute units (one head, a short chunk against a
+ * long cache) cuts each query tile's keys into ranges of about equal size
+ * (up to 32 per tile; attn_prefill_split_plan reports them), computed in
+ * parallel and merged with the guide's output correction, each range taken
+ * as one chunk (as attn_decode_fwd below does for one query).  It allocates
+ * (D + 1) * 4 * B * H * Lq * R bytes the same stream-ordered way, R the
+ * largest range count of a tile.  The environment variable
+ * ATTN_PREFILL_SPLITS=n forces n ranges per tile (capped at 16 and so that
+ * no range is empty; 1 never splits).
  *
  * Returns ATTN_OK or a negative attn_status_t.
  */
