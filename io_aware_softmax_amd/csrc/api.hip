@@ -61,10 +61,14 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 }
 
 // ATTN_PREFILL_KERNEL=single forces the single-group 16-bit prefill kernel
-// everywhere (tests compare the two kernels); read on every call.
+// everywhere, =two the two-group kernel also at D = 64 (tests compare the
+// kernels); read on every call.  0: the library's choice.
 int prefill_variant() {
   const char* e = std::getenv("ATTN_PREFILL_KERNEL");
-  return (e != nullptr && std::strcmp(e, "single") == 0) ? 1 : 0;
+  if (e == nullptr) return 0;
+  if (std::strcmp(e, "single") == 0) return 1;
+  if (std::strcmp(e, "two") == 0) return 2;
+  return 0;
 }
 
 // Key ranges of the two-group prefill: ATTN_PREFILL_SPLITS=n forces n per
@@ -245,6 +249,8 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
   hipError_t e;
   if (dtype == ATTN_F32) {
     e = attn::launch_prefill_f32(D, causal != 0, a, s);
+  } else if (D == 64 && a.c > 0.f && prefill_variant() == 2) {
+    e = attn::launch_prefill_pp(dtype, 64, causal != 0, a, s);
   } else if (D == 128 && a.c > 0.f && prefill_variant() != 1) {
     // Shapes with fewer query tiles than the part has compute units (one
     // head, short chunks) cut each tile's keys into ranges, merged after.
@@ -264,7 +270,7 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
       const hipError_t ef = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = ef;
     } else {
-      e = attn::launch_prefill_pp(dtype, causal != 0, a, s);
+      e = attn::launch_prefill_pp(dtype, 128, causal != 0, a, s);
     }
   } else {
     e = attn::launch_prefill_mfma(dtype, D, causal != 0, a, s);

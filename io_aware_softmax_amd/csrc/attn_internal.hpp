@@ -80,8 +80,8 @@ hipError_t resident_workgroups(int dev, const void* kernel, int block, int* out)
 
 // Tiled one-pass prefill on MFMA for 16-bit inputs (dtype 1 = f16, 2 = bf16).
 hipError_t launch_prefill_mfma(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
-// Two-group (ping-pong) variant of the 16-bit prefill for D = 128.
-hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s);
+// Two-group (ping-pong) variant of the 16-bit prefill, D = 64 or 128.
+hipError_t launch_prefill_pp(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s);
 // Key ranges of a split prefill: query tile qt (256 rows) of every
 // (batch, head) has ranges[qt] contiguous, balanced, non-empty ranges of its
 // 64-key tiles; item[t] = (qt << 5) | range lists the `items` ranges of one
@@ -95,7 +95,7 @@ struct PrefillSplitPlan {
   unsigned short item[kSplitMaxItems];
   unsigned char ranges[kSplitMaxTiles];
 };
-// The same with the keys of every query tile cut as `plan` says (partials in
+// The same (D = 128) with the keys of every query tile cut as `plan` says (partials in
 // part_o [max_ranges, BH, Lq, 128] and part_l [max_ranges, BH, Lq] fp32),
 // then merged.
 hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, const PrefillSplitPlan& plan,

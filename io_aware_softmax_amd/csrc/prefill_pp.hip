@@ -308,6 +308,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // of an uneven split goes first).  Only for whole tiles; the other cases
   // are issued in one go before the phase.
   constexpr int NR = KP::RUNS + VP::RUNS;  // DMA runs per step (K first)
+  constexpr int NSLOT = 2 * T::KSTEPS + 4 * T::DBLK;  // MFMA slots of a matrix phase
+  static_assert(NR <= NSLOT - 4, "every DMA run needs a slot of its own");
   auto dma_hook = [&](const char* kg, char* kdst, const char* vg, char* vdst) __attribute__((always_inline)) {
     return [=, &k_src, &v_src](int i) __attribute__((always_inline)) {
       if (i == 0) {
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       }
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
-        if (i == 2 + q * 28 / NR) {
+        if (i == 2 + q * (NSLOT - 4) / NR) {
           if (q < KP::RUNS) {
             const int i0 = KP::run_first(q);
             dma_run_n(KP::run_len(q), kg, k_src + i0, lds_addr(kdst + KP::inst(i0, wd) * 1024));
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   }
 }
 
-template <bool BF16, bool CAUSAL, bool SPLIT>
+template <bool BF16, int D, bool CAUSAL, bool SPLIT>
 hipError_t launch(const PrefillArgs& a, hipStream_t s, const PrefillSplitPlan& plan, float* part_o, float* part_l) {
   const int nqt = (a.Lq + kRows - 1) / kRows;
   const unsigned qsign = a.neg ? 0x80008000u : 0u;
@@ -584,7 +586,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s, const PrefillSplitPlan& p
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   int resident = 0;
-  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_pp_kernel<BF16, 128, CAUSAL, SPLIT>),
+  e = resident_workgroups(dev, reinterpret_cast<const void*>(&prefill_pp_kernel<BF16, D, CAUSAL, SPLIT>),
                           kThreads, &resident);
   if (e != hipSuccess) return e;
   const int cap = resident / 8 * 8;
@@ -602,7 +604,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t s, const PrefillSplitPlan& p
     slots = 0;
     per = 0;
   }
-  hipLaunchKernelGGL((prefill_pp_kernel<BF16, 128, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((prefill_pp_kernel<BF16, D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const unsigned short*>(a.q), static_cast<const unsigned short*>(a.k),
                      static_cast<const unsigned short*>(a.v), static_cast<unsigned short*>(a.o), a.lse, a.BH, a.Lq,
                      a.Lk, nqt, a.c, qsign, slots, per, part_o, part_l, plan);
@@ -641,24 +643,29 @@ __global__ __launch_bounds__(256) void prefill_split_combine(const float* __rest
 
 }  // namespace
 
-hipError_t launch_prefill_pp(int dtype, bool causal, const PrefillArgs& a, hipStream_t s) {
+template <int D>
+hipError_t launch_unsplit(int dtype, bool causal, const PrefillArgs& a, hipStream_t s) {
   static const PrefillSplitPlan none{};  // not read by the unsplit kernel
   if (dtype == 2)
-    return causal ? launch<true, true, false>(a, s, none, nullptr, nullptr)
-                  : launch<true, false, false>(a, s, none, nullptr, nullptr);
-  return causal ? launch<false, true, false>(a, s, none, nullptr, nullptr)
-                : launch<false, false, false>(a, s, none, nullptr, nullptr);
+    return causal ? launch<true, D, true, false>(a, s, none, nullptr, nullptr)
+                  : launch<true, D, false, false>(a, s, none, nullptr, nullptr);
+  return causal ? launch<false, D, true, false>(a, s, none, nullptr, nullptr)
+                : launch<false, D, false, false>(a, s, none, nullptr, nullptr);
+}
+
+hipError_t launch_prefill_pp(int dtype, int D, bool causal, const PrefillArgs& a, hipStream_t s) {
+  return D == 64 ? launch_unsplit<64>(dtype, causal, a, s) : launch_unsplit<128>(dtype, causal, a, s);
 }
 
 hipError_t launch_prefill_pp_split(int dtype, bool causal, const PrefillArgs& a, const PrefillSplitPlan& plan,
                                    float* part_o, float* part_l, hipStream_t s) {
   hipError_t e;
   if (dtype == 2)
-    e = causal ? launch<true, true, true>(a, s, plan, part_o, part_l)
-               : launch<true, false, true>(a, s, plan, part_o, part_l);
+    e = causal ? launch<true, 128, true, true>(a, s, plan, part_o, part_l)
+               : launch<true, 128, false, true>(a, s, plan, part_o, part_l);
   else
-    e = causal ? launch<false, true, true>(a, s, plan, part_o, part_l)
-               : launch<false, false, true>(a, s, plan, part_o, part_l);
+    e = causal ? launch<false, 128, true, true>(a, s, plan, part_o, part_l)
+               : launch<false, 128, false, true>(a, s, plan, part_o, part_l);
   if (e != hipSuccess) return e;
   const int rows = a.BH * a.Lq;
   if (dtype == 2)

@@ -138,3 +138,43 @@ def test_extended_shapes_sampled_rows(B, H, Lq, Lk, D, dtype, causal):
             vals = {t: inputs.slab_values(wl, t, b, h)[None, None] for t in "qkv"}
             Or, Lr = oracle.attention(vals["q"], vals["k"], vals["v"], wl.scale, causal, rows=rows)
             compare(f"{wl.name} b{b} h{h}", dtype, O[b, h][rows][None, None], L[b, h][rows][None, None], Or, Lr)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Lq,Lk", [(1, 4, 700, 700), (2, 3, 300, 1000), (1, 2, 1000, 300)])
+def test_two_group_d64(B, H, Lq, Lk, dtype, causal, monkeypatch):
+    """The two-group kernel at D = 64 (ATTN_PREFILL_KERNEL=two): ragged query
+    and key tails, Lq < Lk and Lq > Lk, against the oracle and against the
+    single-group kernel on the same inputs."""
+    if causal and Lq > Lk:
+        pytest.skip("causal needs Lq <= Lk in this test (rows without keys are covered elsewhere)")
+    D = 64
+    vals = {"q": _normal((B, H, Lq, D), 900 + Lq), "k": _normal((B, H, Lk, D), 901 + Lk),
+            "v": _normal((B, H, Lk, D), 902 + Lk)}
+    scale = 1.0 / np.sqrt(D)
+    say(f"case two-group D64 {B}x{H} {Lq}x{Lk} {dtype} causal={causal}")
+    monkeypatch.setenv("ATTN_PREFILL_KERNEL", "two")
+    _, O_two = _check(f"two-group D64 {Lq}x{Lk} {dtype} c{int(causal)}", vals, dtype, causal, scale)
+    monkeypatch.setenv("ATTN_PREFILL_KERNEL", "single")
+    _, O_one = _check(f"single-group D64 {Lq}x{Lk} {dtype} c{int(causal)}", vals, dtype, causal, scale)
+    assert np.max(np.abs(O_two - O_one)) <= 2 * O_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_two_group_d64_reference_paths(dtype, monkeypatch):
+    """D = 64 on the two-group kernel: rising row maxima (the reference
+    moves every few tiles) and scale 40 (weights overflow to inf)."""
+    B, H, L, D = 1, 2, 1500, 64
+    q = 0.1 * _normal((B, H, L, D), 611)
+    k = 0.1 * _normal((B, H, L, D), 612)
+    v = _normal((B, H, L, D), 613)
+    q[..., 0] = 1.0
+    k[..., 0] = np.arange(L, dtype=np.float32) * 0.3
+    monkeypatch.setenv("ATTN_PREFILL_KERNEL", "two")
+    say(f"case two-group D64 reference paths {dtype}")
+    for causal in (False, True):
+        _check(f"rising D64 {dtype} c{int(causal)}", {"q": q, "k": k, "v": v}, dtype, causal, 1.0 / np.sqrt(D))
+    vals = {t: _normal((1, 2, 400, D), 710 + i) for i, t in enumerate("qkv")}
+    for causal in (False, True):
+        _check(f"huge D64 {dtype} c{int(causal)}", vals, dtype, causal, 40.0)
