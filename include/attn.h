@@ -100,7 +100,10 @@ typedef enum {
  * (D + 1) * 4 * B * H * Lq * R bytes the same stream-ordered way, R the
  * largest range count of a tile.  The environment variable
  * ATTN_PREFILL_SPLITS=n forces n ranges per tile (capped at 16 and so that
- * no range is empty; 1 never splits).
+ * no range is empty; 1 never splits).  ATTN_PREFILL_KERNEL=single runs every
+ * 16-bit prefill on the single-group kernel, =two runs D = 64 on the
+ * two-group kernel too (by default D = 64 takes the single-group one).
+ * Both variables are read on every call.
  *
  * Returns ATTN_OK or a negative attn_status_t.
  */
