@@ -11,8 +11,9 @@ Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
   that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
 * ``sweep_ext`` - shapes past the five workloads: the fp16 sweep at
   L = 8192, bf16 D128 lengths causal and not, one sequence with one or a few
-  heads (few workgroups), and chunked prefill (Lq new queries against Lk
-  cached keys).  One JSON line per case.
+  heads (few workgroups), the long-context workload's shape (B1 H8 L65536
+  causal), and chunked prefill (Lq new queries against Lk cached keys).  One
+  JSON line per case.
 * ``ex`` - forward and backward of the causal bf16 8k prefill through the
   plain entry points and through attn_fwd_ex / attn_bwd_ex with boolean and
   additive masks and dropout.  One JSON line per case.
@@ -131,8 +132,9 @@ def cmd_sweep(args):
 
 def cmd_sweep_ext(args):
     """Shapes beyond the five workloads: the fp16 sweep at L = 8192, bf16 D = 128
-    lengths, a single sequence and head (few workgroups), and chunked prefill
-    (Lq new queries against Lk cached keys, bottom-right causal)."""
+    lengths, a single sequence and head (few workgroups), the long-context
+    workload's shape (B1 H8 L65536 causal), and chunked prefill (Lq new
+    queries against Lk cached keys, bottom-right causal)."""
     cases = [
         # (label, B, H, Lq, Lk, D, dtype, causal, materialised baseline)
         ("fp16 sweep extension", 4, 8, 8192, 8192, 64, "f16", False, True),
@@ -143,6 +145,7 @@ def cmd_sweep_ext(args):
         ("single sequence, one head", 1, 1, 16384, 16384, 128, "bf16", True, False),
         ("single sequence, one head", 1, 1, 65536, 65536, 128, "bf16", True, False),
         ("single sequence, 8 heads", 1, 8, 16384, 16384, 128, "bf16", True, False),
+        ("long-context causal prefill", 1, 8, 65536, 65536, 128, "bf16", True, False),
         ("chunked prefill", 1, 32, 512, 8192, 128, "bf16", True, False),
         ("chunked prefill", 1, 32, 2048, 8192, 128, "bf16", True, False),
     ]
