@@ -268,6 +268,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
     kreg[t] = __builtin_bit_cast(s16x8, xk);
     vreg[t] = __builtin_bit_cast(s16x8, xv);
   }
+  // Wait for these loads here, before the tile loop: otherwise the compiler
+  // (which does not count the DMA issued by inline assembly) puts a full
+  // vmcnt(0) wait at their first use inside the loop, on every tile, and
+  // that wait also drains the next tile's DMA just issued.
+#pragma unroll
+  for (int t = 0; t < KS; ++t) asm volatile("" ::"v"(kreg[t]), "v"(vreg[t]));
 
   // Per-lane LDS offsets.  Row reads (A operands over D): row perm_row(n),
   // chunk 2 t + h.  Transposed reads (B operands over queries): rows
@@ -288,6 +294,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
     }
 
   const size_t mslab = KIND != 0 ? mask_slab(md, bh, Lq, Lk) : 0;
+  const size_t mask_lane_off = (size_t)(8 * h) * Lk + (unsigned)key;  // lane part of a mask element's index
   const PhiloxKey pk{md.k0, md.k1};
 
   f32x16 dk[DB], dv[DB];
@@ -308,21 +315,30 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
     const float* st = reinterpret_cast<const float*>(stage + 2 * T::BYTES);
     // Mask terms and dropout keep bits do not depend on the products: they
     // come first so that their loads and VALU work overlap the MFMAs.
-    // Mask terms (base 2) of the 16 elements: branch-free loads (elements
-    // outside [0, Lq) x [0, Lk) read element (0, 0) of the slab and get 0).
+    // Mask terms (base 2) of the 16 elements, from branch-free loads.
     float mt[16];
     if constexpr (EX) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt[r] = 0.f;
     }
     if constexpr (KIND != 0) {
+      // Element r is query qb + c + 8 h (c = 16 (r / 8) + r % 8) of key
+      // `key`.  Its mask row starts at a wave-uniform address (row index
+      // clamped to Lq - 1, so in bounds); the lane adds 8 h rows and its key,
+      // or nothing outside [0, Lq) x [0, Lk).  Selects, no multiply under a
+      // lane condition (which compiled to divergent branches).  The term of
+      // an element outside that range is whatever in-bounds byte it read:
+      // a padded query row has lse2 = +inf (weight 0 whatever the term), and
+      // a key past Lk only feeds its own dK / dV row, which is never stored.
+      // (A term that depends on in[r] let the compiler sink a load into a
+      // branch that waited for every load in flight.)
       size_t idx[16];
       bool in[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-        in[r] = qi < Lq && key < Lk;
-        idx[r] = mslab + (in[r] ? (size_t)qi * Lk + key : 0);
+        const int ru = qb + 16 * (r >> 3) + (r & 7);
+        in[r] = ru + 8 * h < Lq && key < Lk;
+        idx[r] = mslab + (size_t)min(ru, Lq - 1) * Lk + (in[r] ? mask_lane_off : 0);
       }
       if constexpr (KIND == 1) {
         const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
@@ -330,14 +346,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = m8[idx[r]];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt[r] = (in[r] && v[r] == 0) ? -INFINITY : 0.f;
+        for (int r = 0; r < 16; ++r) mt[r] = v[r] == 0 ? -INFINITY : 0.f;
       } else {
         const float* m32 = static_cast<const float*>(md.mask);
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[r] = m32[idx[r]];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt[r] = in[r] ? v[r] * kLog2e : 0.f;
+        for (int r = 0; r < 16; ++r) mt[r] = v[r] * kLog2e;
       }
     }
     // Dropout keep bits of the 16 elements (bit r).  Element r needs word
@@ -411,7 +427,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-      float p = mt[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt[r] - l2[r]));
+      // A masked-out element takes exponent -inf (weight 0) by a select
+      // before the exponential: a row with every key masked has lse2 = -inf,
+      // where mt - lse2 would be NaN.
+      const float xe = __builtin_fmaf(s[r], c, mt[r] - l2[r]);
+      float p = __builtin_amdgcn_exp2f(mt[r] == -INFINITY ? -INFINITY : xe);
       if (masked && key > qi + off) p = 0.f;
       // Dropout: the value product sees the kept weights scaled by 1/(1-p),
       // and dP reaches the softmax through the same factors.
@@ -596,6 +616,13 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     l2 = st[qi % BQ];
     dd = st[BQ + qi % BQ];
   }
+  // Wait for these loads here, before the tile loop: otherwise the compiler
+  // (which does not count the DMA issued by inline assembly) puts a full
+  // vmcnt(0) wait at their first use inside the loop, which drains the next
+  // tile's DMA right after its issue, on every tile.
+#pragma unroll
+  for (int t = 0; t < KS; ++t) asm volatile("" ::"v"(qreg[t]), "v"(oreg[t]));
+  asm volatile("" ::"v"(l2), "v"(dd));
   // Row of the lane's query in the mask (row 0 of the slab for padded
   // queries: in bounds, never stored).
   const size_t mrow = KIND != 0 ? mask_slab(md, bh, Lq, Lk) + (size_t)(qi < Lq ? qi : 0) * Lk : 0;
@@ -653,7 +680,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     s16x8 sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = mt[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, mt[r] - l2));
+      const float xe = __builtin_fmaf(s[r], c, mt[r] - l2);  // select before the exponential, as in dK/dV
+      float p = __builtin_amdgcn_exp2f(mt[r] == -INFINITY ? -INFINITY : xe);
       if (masked) {
         const int kj = kb0 + 16 * (r >> 3) + 8 * h + (r & 7);
         if (kj >= Lk || (CAUSAL && kj > qi + off)) p = 0.f;
