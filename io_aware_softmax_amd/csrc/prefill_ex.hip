@@ -89,6 +89,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)qi * D + 16 * t + 8 * h);
     qreg[t] = __builtin_bit_cast(s16x8, x);
   }
+  // Wait for the Q loads here, before the tile loop: otherwise the compiler
+  // (which does not count the DMA issued by inline assembly) puts a full
+  // vmcnt(0) wait at their first use inside the loop, draining the next
+  // tile's DMA just issued.
+#pragma unroll
+  for (int t = 0; t < KS; ++t) asm volatile("" ::"v"(qreg[t]));
   const size_t mrow = KIND != 0 && qi < Lq ? mask_slab(md, bh, Lq, Lk) + (size_t)qi * Lk : 0;
   const PhiloxKey pk{md.k0, md.k1};
 
