@@ -118,7 +118,26 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   float m_run = -INFINITY;  // running maximum (base-2 units), same in both halves
   float l_run = 0.f;        // this half's share of the denominator
 
-  auto tile = [&](const char* stage, int kv0) __attribute__((always_inline)) {
+  // Boolean masks: the raw bytes of a whole, aligned tile are loaded one
+  // tile ahead, before that tile's K/V DMA is issued.  The compiler does not
+  // count the DMA (inline assembly), so waiting for mask loads issued after
+  // it would also wait for the DMA; loaded before it and consumed after the
+  // landing wait, they cost no wait inside the tile.
+  constexpr bool PREF = KIND == 1 && !DROP;  // with dropout: no registers to spare
+  auto raw_load = [&](int kv0, uint2 (&raw)[4]) __attribute__((always_inline)) {
+    if (Lk % 8 == 0 && kv0 + BQ <= Lk) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        raw[grp] = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + mrow + kv0 +
+                                                   32 * (grp >> 1) + 16 * (grp & 1) + 8 * h);
+    }
+  };
+  auto raw_landed = [&](const uint2 (&raw)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) asm volatile("" ::"v"(raw[grp].x), "v"(raw[grp].y));
+  };
+
+  auto tile = [&](const char* stage, int kv0, const uint2 (&raw)[4]) __attribute__((always_inline)) {
     if (kv0 >= w_key_end) return;
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
@@ -128,10 +147,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     const bool vec = Lk % 8 == 0 && whole;     // whole, aligned mask rows for the tile
     float t8[4][8];
     if constexpr (KIND != 0) {
+      if (PREF && vec) {
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
-        mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, vec, t8[grp]);
+        for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            t8[grp][e] = (((e < 4 ? raw[grp].x : raw[grp].y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
+      } else {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
+          mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, vec, t8[grp]);
+        }
       }
     }
     f32x16 s[2];
@@ -219,17 +246,28 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     }
   };
 
+  uint2 rawA[4] = {}, rawB[4] = {};
+  if constexpr (PREF) raw_load(0, rawA);
   land_all();
+  if constexpr (PREF) raw_landed(rawA);
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
+    if constexpr (PREF) {
+      if (j + 1 < nkt) raw_load((j + 1) * BQ, rawB);
+    }
     if (j + 1 < nkt) issue(j + 1, smem + STAGE);
-    tile(smem, j * BQ);
+    tile(smem, j * BQ, rawA);
     land_all();
+    if constexpr (PREF) raw_landed(rawB);
     __syncthreads();
     if (j + 1 >= nkt) break;
+    if constexpr (PREF) {
+      if (j + 2 < nkt) raw_load((j + 2) * BQ, rawA);
+    }
     if (j + 2 < nkt) issue(j + 2, smem);
-    tile(smem + STAGE, (j + 1) * BQ);
+    tile(smem + STAGE, (j + 1) * BQ, rawB);
     land_all();
+    if constexpr (PREF) raw_landed(rawA);
     __syncthreads();
   }
 
