@@ -305,8 +305,40 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
   }
   const float c = a.c;
 
-  // One 32-query block b of the tile in `stage`.
-  auto block = [&](const char* stage, int q0, int b) __attribute__((always_inline)) {
+  // Index of mask element r of the 32-query block starting at query qb:
+  // query qb + c + 8 h (c = 16 (r / 8) + r % 8) of key `key`.  The row
+  // starts at a wave-uniform address (row index clamped to Lq - 1, so in
+  // bounds); the lane adds 8 h rows and its key, or nothing outside
+  // [0, Lq) x [0, Lk).  Selects, no multiply under a lane condition (which
+  // compiled to divergent branches).
+  auto mask_idx = [&](int qb, int r) __attribute__((always_inline)) -> size_t {
+    const int ru = qb + 16 * (r >> 3) + (r & 7);
+    const bool in = ru + 8 * h < Lq && key < Lk;
+    return mslab + (size_t)min(ru, Lq - 1) * Lk + (in ? mask_lane_off : 0);
+  };
+  // Boolean masks: the 32 bytes of a tile's two blocks are loaded one tile
+  // ahead, before that tile's Q / dO DMA is issued.  The compiler does not
+  // count the DMA (inline assembly), so waiting for mask loads issued after
+  // it would also wait for the DMA; loaded before it and consumed after the
+  // landing wait, they cost no wait inside the tile.
+  constexpr bool PREF = KIND == 1;
+  auto mask_prefetch = [&](int q0, unsigned char (&m)[2][16]) __attribute__((always_inline)) {
+    const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m[b][r] = m8[mask_idx(q0 + 32 * b, r)];
+  };
+  auto mask_landed = [&](const unsigned char (&m)[2][16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("" ::"v"((unsigned)m[b][r]));
+  };
+
+  // One 32-query block b of the tile in `stage` (mraw: its prefetched
+  // boolean mask bytes).
+  auto block = [&](const char* stage, int q0, int b, const unsigned char (&mraw)[16]) __attribute__((always_inline)) {
     const int qb = q0 + 32 * b;
     if (qb >= Lq) return;
     if (CAUSAL && qb + 31 + off < kw0) return;  // no query of the block sees a key of the wave
@@ -322,36 +354,20 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       for (int r = 0; r < 16; ++r) mt[r] = 0.f;
     }
     if constexpr (KIND != 0) {
-      // Element r is query qb + c + 8 h (c = 16 (r / 8) + r % 8) of key
-      // `key`.  Its mask row starts at a wave-uniform address (row index
-      // clamped to Lq - 1, so in bounds); the lane adds 8 h rows and its key,
-      // or nothing outside [0, Lq) x [0, Lk).  Selects, no multiply under a
-      // lane condition (which compiled to divergent branches).  The term of
-      // an element outside that range is whatever in-bounds byte it read:
-      // a padded query row has lse2 = +inf (weight 0 whatever the term), and
-      // a key past Lk only feeds its own dK / dV row, which is never stored.
-      // (A term that depends on in[r] let the compiler sink a load into a
-      // branch that waited for every load in flight.)
-      size_t idx[16];
-      bool in[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ru = qb + 16 * (r >> 3) + (r & 7);
-        in[r] = ru + 8 * h < Lq && key < Lk;
-        idx[r] = mslab + (size_t)min(ru, Lq - 1) * Lk + (in[r] ? mask_lane_off : 0);
-      }
+      // The term of an element outside [0, Lq) x [0, Lk) is whatever
+      // in-bounds byte it read (mask_idx): a padded query row has
+      // lse2 = +inf (weight 0 whatever the term), and a key past Lk only
+      // feeds its own dK / dV row, which is never stored.  (A term that
+      // depends on the range flag let the compiler sink a load into a branch
+      // that waited for every load in flight.)
       if constexpr (KIND == 1) {
-        const unsigned char* m8 = static_cast<const unsigned char*>(md.mask);
-        unsigned char v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = m8[idx[r]];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt[r] = v[r] == 0 ? -INFINITY : 0.f;
+        for (int r = 0; r < 16; ++r) mt[r] = mraw[r] == 0 ? -INFINITY : 0.f;
       } else {
         const float* m32 = static_cast<const float*>(md.mask);
         float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v[r] = m32[idx[r]];
+        for (int r = 0; r < 16; ++r) v[r] = m32[mask_idx(qb, r)];
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt[r] = v[r] * kLog2e;
       }
@@ -478,7 +494,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
   // fetches the current tile again into the idle stage (never read).  Other
   // tiles (causal diagonal, Lq tail) issue the next tile's DMA first and go
   // block by block.
-  auto tile = [&](char* stage, int q0, char* nstage, int tn) __attribute__((always_inline)) {
+  auto tile = [&](char* stage, int q0, char* nstage, int tn, const unsigned char (&mcur)[2][16],
+                  unsigned char (&mnext)[2][16]) __attribute__((always_inline)) {
     const bool has_next = tn < nqt;
     if (!EX && q0 + BQ <= Lq && (!CAUSAL || q0 + off >= kw0 + 31)) {
       const int tf = has_next ? tn : tn - 1;
@@ -512,23 +529,31 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       dkdv_tile_fast<BF16, D>(stage, stage + T::BYTES, reinterpret_cast<const float*>(stage + 2 * T::BYTES), kreg,
                               vreg, dk, dv, ra, ta, h, c, hook);
     } else {
+      if constexpr (PREF) {
+        if (has_next) mask_prefetch(tn * BQ, mnext);
+      }
       if (has_next) issue(tn, nstage);
-      block(stage, q0, 0);
-      block(stage, q0, 1);
+      block(stage, q0, 0, mcur[0]);
+      block(stage, q0, 1, mcur[1]);
     }
   };
 
+  unsigned char mA[2][16] = {}, mB[2][16] = {};
+  if constexpr (PREF) mask_prefetch(t_begin * BQ, mA);
   land_all();
+  if constexpr (PREF) mask_landed(mA);
   __syncthreads();
   // Tiles alternate between the two stages; the loop body covers a pair so
   // that every LDS address is a lane offset plus an immediate.
   for (int t = t_begin; t < nqt; t += 2) {
-    tile(smem, t * BQ, smem + STAGE, t + 1);
+    tile(smem, t * BQ, smem + STAGE, t + 1, mA, mB);
     land_all();
+    if constexpr (PREF) mask_landed(mB);
     __syncthreads();
     if (t + 1 >= nqt) break;
-    tile(smem + STAGE, (t + 1) * BQ, smem, t + 2);
+    tile(smem + STAGE, (t + 1) * BQ, smem, t + 2, mB, mA);
     land_all();
+    if constexpr (PREF) mask_landed(mA);
     __syncthreads();
   }
 
