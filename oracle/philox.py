@@ -14,8 +14,10 @@ rounds.  One round multiplies words 0 and 2 by the constants M0, M1 (full
 
 and the key is bumped by the Weyl constants (W0, W1) between rounds.  The
 function is generic in the word width: the 64-bit instance is pinned against
-NumPy's own Philox bit generator (same round structure and key schedule),
-the 32-bit instance is the one dropout uses.
+NumPy's own Philox bit generator (same round structure and key schedule);
+the 32-bit instance, the one dropout uses, is pinned to the published
+Philox4x32-10 known-answer vectors of the Random123 library that accompanies
+the paper.
 
 Dropout reading (the comfyai.app chapter "6.3 FlashAttention" lists dropout
 between the softmax and the value product of the fused tile, section 6.3.3,

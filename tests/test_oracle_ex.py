@@ -1,8 +1,10 @@
 """Pins of the masked / dropout oracle (``attention_ex``, ``attention_ex_bwd``)
 and of its counter-based generator (``oracle/philox.py``).  CPU only.
 
-* Philox: the round structure and key schedule, run at 64-bit width, equal
-  NumPy's Philox4x64-10 bit generator block for block; the vectorised
+* Philox: the 32-bit instance equals the published Philox4x32-10
+  known-answer vectors (``tests/golden/philox4x32_10_kat.txt``); the round
+  structure and key schedule, run at 64-bit width, equal NumPy's
+  Philox4x64-10 bit generator block for block; the vectorised
   32-bit evaluation equals the scalar one; the 32-bit words are uniform
   (mean, per-bit frequencies) and a one-bit change of the counter flips
   about half of the output bits.
@@ -21,6 +23,7 @@ and of its counter-based generator (``oracle/philox.py``).  CPU only.
 """
 
 import sys
+from pathlib import Path
 
 import numpy as np
 import pytest
@@ -35,6 +38,47 @@ _KEEP = ph.keep_pattern  # the pins use this reference, never a patched one
 
 
 # ---------------------------------------------------------------- Philox --
+
+KAT = Path(__file__).parent / "golden" / "philox4x32_10_kat.txt"
+
+
+def _kat_rows():
+    rows = []
+    for line in KAT.read_text().splitlines():
+        if line.startswith("#") or not line.strip():
+            continue
+        lhs, rhs = line.split(":")
+        rows.append(([int(w, 16) for w in lhs.split()], [int(w, 16) for w in rhs.split()]))
+    return rows
+
+
+def test_philox32_known_answers():
+    """The 32-bit instance (multipliers, Weyl constants, round structure)
+    against the published Philox4x32-10 known-answer vectors, through both
+    the scalar and the vectorised form."""
+    rows = _kat_rows()
+    assert len(rows) == 3
+    for words, expect in rows:
+        ctr, key = words[:4], words[4:]
+        assert [int(x) for x in ph.philox4x32(*ctr, *key)] == expect, words
+        assert ph.philox(ctr, key, 32, ph.M4x32, ph.W4x32) == expect, words
+
+
+def test_keep_pattern_reads_the_known_answer_words():
+    """keep_pattern takes word (j mod 4) of the block with counter
+    (j / 4, i, bh, offset) and key (seed low, seed high): with the all-zero
+    KAT counter and key (block 0 of row 0, bh 0, offset 0, seed 0) the four
+    keys see exactly that vector's four words."""
+    words, expect = _kat_rows()[0]
+    assert words == [0] * 6
+    for w in expect:
+        # p just above w / 2^32: words <= w are dropped, larger ones kept.
+        p = float(np.nextafter(np.float32(w / 2.0 ** 32), np.float32(1.0)))
+        thr = ph.dropout_threshold(p)
+        assert thr > w
+        keep = ph.keep_pattern(0, 0, 0, [0], 4, p)[0]
+        assert list(keep) == [x >= thr for x in expect]
+
 
 @pytest.mark.parametrize("key", [(1, 2), (0, 0), (0xDEADBEEFCAFEF00D, 0x0123456789ABCDEF)])
 def test_philox64_matches_numpy(key):
