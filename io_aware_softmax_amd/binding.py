@@ -105,24 +105,100 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream)
 
 
-def _prep(q, k, v, out, lse, Lq):
+def _is_tensor(t) -> bool:
+    return isinstance(t, torch.Tensor)
+
+
+def _dims(q):
+    """(B, H, Lq, D) of q, which must be a 4-d tensor."""
+    if not _is_tensor(q) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, L, D] tensor")
+    return tuple(q.shape)
+
+
+def _keys(k):
+    """Lk of k, which must be a 4-d tensor."""
+    if not _is_tensor(k) or k.dim() != 4:
+        raise ValueError("k must be a [B, H, L, D] tensor")
+    return k.shape[2]
+
+
+def _prep(q, k, v, out, lse, Lq, place=True):
+    """Check q, k, v (and a caller's out / lse) against the shapes the C ABI
+    takes from q.shape and k.shape: the kernels trust those sizes, so any
+    mismatch here would become an out-of-bounds access on the device.
+    Structure (shape, dtype, layout) is checked before placement so the
+    messages name the first real problem; place=False leaves the device
+    check to the caller (which checks more tensors first).  Returns
+    (out, lse), allocated when not given (place=True only)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        if not _is_tensor(t):
+            raise ValueError(f"{name} must be a torch tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, L, D]")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if q.dtype not in _DTYPE_CODES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one of float32, float16, bfloat16")
-    B, H, _, D = q.shape
+    B, H, Lq_q, D = q.shape
+    if Lq_q != Lq:
+        raise ValueError(f"q must have {Lq} queries per (batch, head)")
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("k must be [B, H, Lk, D] with q's B, H and D")
+    if v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    if out is not None:
+        if not _is_tensor(out) or tuple(out.shape) != (B, H, Lq, D) or out.dtype != q.dtype:
+            raise ValueError("out must be [B, H, Lq, D] with q's dtype")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    if lse is not None:
+        if not _is_tensor(lse) or tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32:
+            raise ValueError("lse must be a float32 tensor [B, H, Lq]")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous")
+    if not place:
+        return out, lse
+    _same_gpu(q, ("k", k), ("v", v), ("out", out), ("lse", lse))
     if out is None:
         out = torch.empty((B, H, Lq, D), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    if not out.is_contiguous() or not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise ValueError("out and lse must be contiguous (lse float32)")
     return out, lse
+
+
+def _same_gpu(q, *named):
+    """q is a GPU tensor and every other (non-None) tensor is on q's device."""
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    for name, t in named:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be a GPU tensor on q's device ({q.device})")
+
+
+def _bwd_prep(q, k, v, out, lse, dout, dq, dk, dv):
+    """Checks of the backward entry points (beyond _prep's): out and dout
+    shaped and typed like q, lse [B, H, Lq] float32, and caller-supplied
+    gradients shaped and typed like their inputs, all on q's device.
+    Returns (dq, dk, dv), allocated when not given."""
+    _prep(q, k, v, out, lse, _dims(q)[2], place=False)
+    if out is None or lse is None:
+        raise ValueError("out and lse (the forward's outputs) are required")
+    if not _is_tensor(dout) or dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must be shaped and typed like q")
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            continue
+        if not _is_tensor(t) or t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like its input")
+    _same_gpu(q, ("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk),
+              ("dv", dv))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    return dq, dk, dv
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
@@ -136,8 +212,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = F
     torch's current stream).
     """
     lib = load()
-    B, H, Lq, D = q.shape
-    Lk = k.shape[2]
+    B, H, Lq, D = _dims(q)
+    Lk = _keys(k)
     out, lse = _prep(q, k, v, out, lse, Lq)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -154,10 +230,10 @@ def attn_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Op
     q [B,H,1,D]; ``num_splits`` 0 lets the library choose.
     """
     lib = load()
-    B, H, Lq, D = q.shape
+    B, H, Lq, D = _dims(q)
     if Lq != 1:
         raise ValueError("attn_decode_fwd takes one query per (batch, head)")
-    Lk = k.shape[2]
+    Lk = _keys(k)
     out, lse = _prep(q, k, v, out, lse, 1)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_decode_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -177,14 +253,15 @@ def attn_decode_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, se
     (each clamped to [0, Lk_max] by the library).
     """
     lib = load()
-    B, H, Lq, D = q.shape
+    B, H, Lq, D = _dims(q)
     if Lq != 1:
         raise ValueError("attn_decode_varlen_fwd takes one query per (batch, head)")
-    if (not isinstance(seqlens, torch.Tensor) or not seqlens.is_cuda or seqlens.dtype != torch.int32
-            or seqlens.shape != (B,) or not seqlens.is_contiguous()):
-        raise ValueError("seqlens must be a contiguous int32 GPU tensor of shape [B]")
-    Lk = k.shape[2]
+    if (not _is_tensor(seqlens) or seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,)
+            or not seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 tensor of shape [B]")
+    Lk = _keys(k)
     out, lse = _prep(q, k, v, out, lse, 1)
+    _same_gpu(q, ("seqlens", seqlens))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_decode_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), seqlens.data_ptr(), B, H, Lk, D, scale,
@@ -203,22 +280,9 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     ``out`` (same shape and dtype).  float16 / bfloat16 only.
     """
     lib = load()
-    B, H, Lq, D = q.shape
-    Lk = k.shape[2]
-    _prep(q, k, v, out, lse, Lq)
-    for name, t in (("out", out), ("dout", dout)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a GPU tensor shaped and typed like q")
-    if not dout.is_contiguous():
-        raise ValueError("dout must be contiguous")
-    if lse.shape != (B, H, Lq):
-        raise ValueError("lse must be [B, H, Lq]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous GPU tensor shaped and typed like its input")
+    dq, dk, dv = _bwd_prep(q, k, v, out, lse, dout, dq, dk, dv)
+    B, H, Lq, D = _dims(q)
+    Lk = _keys(k)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,
@@ -226,13 +290,14 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tenso
     return dq, dk, dv
 
 
-def _mask_args(mask, B, H, Lq, Lk):
+def _mask_args(mask, q, B, H, Lq, Lk):
     """(pointer, kind, mask_b, mask_h) of an optional mask tensor: bool or
-    uint8 -> boolean mask, float32 -> additive mask; shape [1|B, 1|H, Lq, Lk]."""
+    uint8 -> boolean mask, float32 -> additive mask; shape [1|B, 1|H, Lq, Lk]
+    on q's device."""
     if mask is None:
         return None, ATTN_MASK_NONE, 1, 1
-    if not isinstance(mask, torch.Tensor) or not mask.is_cuda or not mask.is_contiguous() or mask.dim() != 4:
-        raise ValueError("mask must be a contiguous 4-d GPU tensor")
+    if not _is_tensor(mask) or not mask.is_contiguous() or mask.dim() != 4:
+        raise ValueError("mask must be a contiguous 4-d tensor")
     if mask.dtype in (torch.bool, torch.uint8):
         kind = ATTN_MASK_BOOL
     elif mask.dtype == torch.float32:
@@ -240,8 +305,9 @@ def _mask_args(mask, B, H, Lq, Lk):
     else:
         raise ValueError("mask dtype must be bool, uint8 (keep / drop) or float32 (additive)")
     mb, mh, mq, mk = mask.shape
-    if mq != Lq or mk != Lk:
+    if mq != Lq or mk != Lk or mb not in (1, B) or mh not in (1, H):
         raise ValueError("mask must be [1 or B, 1 or H, Lq, Lk]")
+    _same_gpu(q, ("mask", mask))
     return mask.data_ptr(), kind, mb, mh
 
 
@@ -257,10 +323,11 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     ``offset`` (32-bit).  float16 / bfloat16 only.
     """
     lib = load()
-    B, H, Lq, D = q.shape
-    Lk = k.shape[2]
+    B, H, Lq, D = _dims(q)
+    Lk = _keys(k)
+    _prep(q, k, v, out, lse, Lq, place=False)
+    mp, kind, mb, mh = _mask_args(mask, q, B, H, Lq, Lk)
     out, lse = _prep(q, k, v, out, lse, Lq)
-    mp, kind, mb, mh = _mask_args(mask, B, H, Lq, Lk)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Lq, Lk,
                            D, int(bool(causal)), scale, mp, kind, mb, mh, float(dropout_p), int(seed), int(offset),
@@ -275,18 +342,10 @@ def attn_bwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
                 dv: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dq, dk, dv of ``attn_fwd_ex`` (same mask and dropout arguments)."""
     lib = load()
-    B, H, Lq, D = q.shape
-    Lk = k.shape[2]
-    _prep(q, k, v, out, lse, Lq)
-    for name, t in (("out", out), ("dout", dout)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be a GPU tensor shaped and typed like q")
-    if not dout.is_contiguous():
-        raise ValueError("dout must be contiguous")
-    mp, kind, mb, mh = _mask_args(mask, B, H, Lq, Lk)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq, dk, dv = _bwd_prep(q, k, v, out, lse, dout, dq, dk, dv)
+    B, H, Lq, D = _dims(q)
+    Lk = _keys(k)
+    mp, kind, mb, mh = _mask_args(mask, q, B, H, Lq, Lk)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Lq, Lk, D,

@@ -178,3 +178,74 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         binding.attn_fwd(x, x, x)
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def _expect_value_error(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_rejects_mismatched_shapes():
+    """Every size the C ABI takes from q.shape and k.shape is checked against
+    the other tensors before any pointer is passed on: a shorter v, or a k
+    with another B, H or D, would make the kernels read past the end of a
+    buffer, and a wrong out / lse would make them write past it.  The checks
+    run before the device check, so CPU tensors reach them here."""
+    import torch
+    q, k, v = _cpu(2, 3, 16, 64), _cpu(2, 3, 20, 64), _cpu(2, 3, 20, 64)
+    f = binding.attn_fwd
+    _expect_value_error(lambda: f(q, k, _cpu(2, 3, 19, 64)), "v must have the shape of k")
+    _expect_value_error(lambda: f(q, _cpu(2, 3, 20, 32), _cpu(2, 3, 20, 32)), "k must be")
+    _expect_value_error(lambda: f(q, _cpu(1, 3, 20, 64), _cpu(1, 3, 20, 64)), "k must be")
+    _expect_value_error(lambda: f(q, _cpu(2, 2, 20, 64), _cpu(2, 2, 20, 64)), "k must be")
+    _expect_value_error(lambda: f(q, k, v, out=_cpu(2, 3, 15, 64)), "out must be")
+    _expect_value_error(lambda: f(q, k, v, out=_cpu(2, 3, 16, 64, dtype=torch.float16)), "out must be")
+    _expect_value_error(lambda: f(q, k, v, lse=_cpu(2, 3, 17, dtype=torch.float32)), "lse must be")
+    _expect_value_error(lambda: f(q, k, v, lse=_cpu(2, 3, 16)), "lse must be")
+    _expect_value_error(lambda: f(q, k.half(), v), "share one of")
+    _expect_value_error(lambda: f(q[:, :, :, :3], k, v), "q must be")
+    _expect_value_error(lambda: f(q.transpose(2, 3), k, v), "contiguous")
+    _expect_value_error(lambda: f(q, k, v), "GPU tensor")  # everything consistent: only the device is wrong
+    # decode entry points
+    q1 = _cpu(2, 3, 1, 64)
+    _expect_value_error(lambda: binding.attn_decode_fwd(q1, k, _cpu(2, 3, 21, 64)), "v must have the shape of k")
+    _expect_value_error(lambda: binding.attn_decode_fwd(q, k, v), "one query")
+    sl = torch.zeros(2, dtype=torch.int32)
+    _expect_value_error(lambda: binding.attn_decode_varlen_fwd(q1, k, v, torch.zeros(3, dtype=torch.int32)),
+                        "seqlens")
+    _expect_value_error(lambda: binding.attn_decode_varlen_fwd(q1, k, _cpu(2, 3, 20, 128), sl), "v must have")
+    _expect_value_error(lambda: binding.attn_decode_varlen_fwd(q1, k, v, sl), "GPU tensor")
+
+
+def test_binding_backward_checks():
+    """attn_bwd and attn_bwd_ex apply the same checks: out / dout like q, lse
+    [B, H, Lq] float32, caller gradients like their inputs."""
+    import torch
+    q, k, v = _cpu(2, 3, 16, 64), _cpu(2, 3, 20, 64), _cpu(2, 3, 20, 64)
+    o, do, lse = _cpu(2, 3, 16, 64), _cpu(2, 3, 16, 64), _cpu(2, 3, 16, dtype=torch.float32)
+    for fn in (binding.attn_bwd, binding.attn_bwd_ex):
+        _expect_value_error(lambda: fn(q, k, _cpu(2, 3, 19, 64), o, lse, do), "v must have the shape of k")
+        _expect_value_error(lambda: fn(q, k, v, _cpu(2, 3, 15, 64), lse, do), "out must be")
+        _expect_value_error(lambda: fn(q, k, v, o, _cpu(2, 3, 15, dtype=torch.float32), do), "lse must be")
+        _expect_value_error(lambda: fn(q, k, v, o, lse, _cpu(2, 3, 16, 32)), "dout must be")
+        _expect_value_error(lambda: fn(q, k, v, o, lse, do, dq=_cpu(2, 3, 20, 64)), "dq must be")
+        _expect_value_error(lambda: fn(q, k, v, o, lse, do, dk=_cpu(2, 3, 16, 64)), "dk must be")
+        _expect_value_error(lambda: fn(q, k, v, o, lse, do, dv=_cpu(2, 3, 20, 64, dtype=torch.float16)), "dv must be")
+        _expect_value_error(lambda: fn(q, k, v, o, None, do), "required")
+        _expect_value_error(lambda: fn(q, k, v, o, lse, do), "GPU tensor")
+
+
+def test_binding_mask_checks():
+    import torch
+    q, k, v = _cpu(2, 3, 16, 64), _cpu(2, 3, 20, 64), _cpu(2, 3, 20, 64)
+    f = binding.attn_fwd_ex
+    _expect_value_error(lambda: f(q, k, v, mask=torch.ones(2, 3, 16, 19, dtype=torch.bool)), "mask must be")
+    _expect_value_error(lambda: f(q, k, v, mask=torch.ones(3, 1, 16, 20, dtype=torch.bool)), "mask must be")
+    _expect_value_error(lambda: f(q, k, v, mask=torch.ones(1, 2, 16, 20, dtype=torch.bool)), "mask must be")
+    _expect_value_error(lambda: f(q, k, v, mask=torch.ones(1, 1, 16, 20, dtype=torch.float16)), "mask dtype")
+    _expect_value_error(lambda: f(q, k, v, mask=torch.ones(1, 1, 16, 20, dtype=torch.bool)), "GPU tensor")
