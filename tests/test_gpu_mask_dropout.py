@@ -12,6 +12,8 @@ LSE = -inf); backward max |x - x_ref| <= 4 u max |x_ref| (u = 2^-8 bf16,
 2^-11 fp16) as for the plain backward.
 """
 
+import functools
+
 import numpy as np
 import pytest
 
@@ -86,6 +88,32 @@ def test_bool_mask(dtype, D, causal):
     B, H, Lq, Lk = 2, 2, 200, 333
     mask = inputs.bool_mask(10 + D, (1, H, Lq, Lk), keep=0.6, empty_rows=3)
     _case(f"bool_{dtype}_D{D}_c{int(causal)}", B, H, Lq, Lk, D, dtype, causal, seed=20 + D, mask=mask, kind="bool")
+
+
+# Boolean masks without dropout at Lk % 8 == 0: the forward loads the mask
+# bytes of a whole aligned tile one tile ahead, and the dQ kernel reads whole
+# aligned blocks as vectors.  Lk 256 and 512 are whole key tiles; 264 is
+# aligned with a ragged last tile (element loads there).
+ALIGNED_BOOL = ([(512, D, dtype, causal) for D in (64, 128) for dtype in ("f16", "bf16") for causal in (False, True)]
+                + [(Lk, D, "bf16", causal) for Lk in (256, 264) for D in (64, 128) for causal in (False, True)])
+
+
+@pytest.mark.parametrize("Lk,D,dtype,causal", ALIGNED_BOOL)
+def test_bool_mask_aligned_no_dropout(Lk, D, dtype, causal):
+    B, H, Lq = 2, 2, 200
+    mshape = (B, H, Lq, Lk) if Lk == 264 else (1, H, Lq, Lk)
+    mask = inputs.bool_mask(Lk + D, mshape, keep=0.6, empty_rows=3)
+    _case(f"bool_al_{Lk}_{dtype}_D{D}_c{int(causal)}", B, H, Lq, Lk, D, dtype, causal, seed=Lk + D + int(causal),
+          mask=mask, kind="bool")
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_additive_mask_aligned_no_dropout(D, dtype, causal):
+    B, H, Lq, Lk = 2, 2, 200, 512
+    mask = inputs.additive_mask(90 + D, (1, H, Lq, Lk), neg_inf=0.2)
+    _case(f"add_al_{dtype}_D{D}_c{int(causal)}", B, H, Lq, Lk, D, dtype, causal, seed=91 + D, mask=mask,
+          kind="add")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -203,3 +231,90 @@ def _case_scaled(name, B, H, Lq, Lk, D, dtype, causal, seed, mask, kind, p, scal
         rel = float(np.max(np.abs(g - r))) / max(float(np.max(np.abs(r))), 1e-30)
         say(f"  {name} {tname}: ratio {rel:.3e} (tol {TAU[dtype]:.2e})")
         assert rel <= TAU[dtype], f"{name}: {tname} {rel}"
+
+
+# The causal bf16 8k workload (q x8 on heads 0-3) with the masks and dropout
+# the masked-forward measurement times: a boolean mask keeping half the keys
+# of every row (broadcast over batch and heads), an additive N(0, 4) mask,
+# dropout 0.1, and the boolean mask with dropout 0.1.  Forward on seeded
+# sampled rows of every head (the same rows in each head, plus the first
+# rows and the tile and diagonal boundaries).
+C3_EX_CASES = {
+    "bool mask": ("bool", 0.0),
+    "additive mask": ("add", 0.0),
+    "dropout 0.1": (None, 0.1),
+    "bool mask + dropout 0.1": ("bool", 0.1),
+}
+
+
+@functools.lru_cache(maxsize=1)
+def _c3_inputs():
+    wl = inputs.WORKLOADS["causal_bf16_8k"]
+    return wl, inputs.generate(wl, ("q", "k", "v", "do"))
+
+
+@functools.lru_cache(maxsize=2)
+def _c3_mask(kind, L):
+    """Drawn once per kind (about 15 s for 8192 x 8192 on the host)."""
+    if kind == "bool":
+        return inputs.bool_mask(5, (1, 1, L, L), keep=0.5)
+    if kind == "add":
+        return inputs.additive_mask(6, (1, 1, L, L), neg_inf=0.0)
+    return None
+
+
+@pytest.mark.parametrize("case", list(C3_EX_CASES))
+def test_c3_shape_masked_forward_sampled_rows(case):
+    import torch
+    from io_aware_softmax_amd import binding
+    kind, p = C3_EX_CASES[case]
+    wl, bits = _c3_inputs()
+    L = wl.Lq
+    mask = _c3_mask(kind, L)
+    q, k, v = (to_device(bits[t], "bf16") for t in "qkv")
+    say(f"case c3 shape, {case}: B{wl.B} H{wl.H} L{L} D{wl.D} causal, 128 sampled rows per head")
+    O, Lse = binding.attn_fwd_ex(q, k, v, causal=True, scale=wl.scale, mask=_mask_tensor(mask), dropout_p=p,
+                                 seed=3)
+    torch.cuda.synchronize()
+    O, Lse = to_host_f64(O), to_host_f64(Lse)
+    rows = np.unique(np.concatenate([inputs.sample_rows(wl, 0, 112),
+                                     [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 4095, 4096, 8190, 8191]]))
+    vals = {t: inputs.to_float32(bits[t], "bf16") for t in "qkv"}
+    Or, Lr = oracle.attention_ex(vals["q"], vals["k"], vals["v"], wl.scale, True, mask=mask, mask_kind=kind,
+                                 dropout_p=p, seed=3, offset=0, rows=rows)
+    Og, Lg = O[:, :, rows], Lse[:, :, rows]
+    empty = np.isneginf(Lr)
+    assert np.all(Og[empty] == 0) and np.all(np.isneginf(Lg[empty])), "rows without keys"
+    compare(f"c3 {case}", "bf16", Og[~empty], Lg[~empty], Or[~empty], Lr[~empty])
+    del O, Lse, q, k, v
+    torch.cuda.empty_cache()
+
+
+def test_c3_shape_bool_mask_backward_full_heads():
+    """attn_bwd_ex at the causal bf16 8k shape with the half-keep boolean
+    mask: dQ, dK, dV of two whole heads (one with x8 queries) against the
+    oracle's chain rule."""
+    import torch
+    from io_aware_softmax_amd import binding
+    wl, bits = _c3_inputs()
+    L = wl.Lq
+    mask = _c3_mask("bool", L)
+    mt = _mask_tensor(mask)
+    q, k, v, do = (to_device(bits[t], "bf16") for t in ("q", "k", "v", "do"))
+    say(f"case c3 shape, bool mask backward: B{wl.B} H{wl.H} L{L}, heads 1 and 17 in full")
+    O, Lse = binding.attn_fwd_ex(q, k, v, causal=True, scale=wl.scale, mask=mt)
+    grads = binding.attn_bwd_ex(q, k, v, O, Lse, do, causal=True, scale=wl.scale, mask=mt)
+    torch.cuda.synchronize()
+    grads = [to_host_f64(g) for g in grads]
+    for h in (1, 17):
+        vals = {t: inputs.to_float32(bits[t][:, h:h + 1], "bf16") for t in ("q", "k", "v", "do")}
+        ref = oracle.attention_ex_bwd(vals["q"], vals["k"], vals["v"], vals["do"], wl.scale, True, mask=mask,
+                                      mask_kind="bool")
+        for tname, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+            gh = g[:, h:h + 1]
+            assert np.all(np.isfinite(gh)), f"non-finite {tname}"
+            rel = float(np.max(np.abs(gh - r))) / float(np.max(np.abs(r)))
+            say(f"  c3 bool bwd h{h} {tname}: ratio {rel:.3e} (tol {TAU['bf16']:.2e})")
+            assert rel <= TAU["bf16"], f"h{h} {tname} {rel}"
+    del grads, q, k, v, do, O, Lse
+    torch.cuda.empty_cache()
