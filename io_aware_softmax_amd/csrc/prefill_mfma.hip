@@ -288,6 +288,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   // lane's part of the denominator s, both relative to that reference.
   float m_ref = -INFINITY;
   float l_run = 0.f;
+  // bf16: sum over tiles of the rounding error (fp32 weight minus its bf16
+  // value) of the row's largest weight of the tile, half in each lane of
+  // the row.  The value product takes the rounded weights, so O is divided
+  // by l_run - e_run: the dominant weight then has the same rounding in the
+  // numerator and the denominator.  LSE keeps the unrounded sum.
+  float e_run = 0.f;
+  float m_cur = -INFINITY;  // maximum (base-2 scaled) of the tile whose weights come next
 
   // Tile row read by this lane for S^T: bits 2 and 3 of n swapped, so the
   // accumulator register r of block blk holds key 32 blk + 16 (r/8) + 8 h + r%8.
@@ -351,8 +358,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
       m_ref = m_new;
       l_run *= alpha;
+      if constexpr (BF16) e_run *= alpha;
 #pragma unroll
       for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
+    }
+  };
+  // Rounding error of the largest weight of a tile with maximum m_tile,
+  // weights taken against m_use (half of it: both lanes of the row add it).
+  auto add_round_error = [&](float m_tile, float m_use) {
+    if constexpr (BF16) {
+      const float wmax = __builtin_amdgcn_exp2f(m_tile - m_use);
+      const float wr = __builtin_bit_cast(float, (unsigned)round16<true>(wmax) << 16);
+      e_run += 0.5f * (wmax - wr);
     }
   };
   // P = exp(a - d), rounded to the MFMA type for the value product; the
@@ -403,7 +420,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   if (w_nkv > 0) {
     scores(sa, kb0);
     if (j_mask == 0) live_a = mask_scores(sa, 0);
-    advance_max(row_max(sa));
+    m_cur = row_max(sa);
+    advance_max(m_cur);
   }
   __syncthreads();  // kb0 is refilled with K_2 in step 0
 
@@ -456,7 +474,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
         m_next = row_max(sn);
       }
     }
+    if (do_cur) add_round_error(m_cur, (m_ref == -INFINITY) ? 0.f : m_ref);
     if (do_next) advance_max(m_next);
+    m_cur = do_next ? m_next : -INFINITY;
     if (j + 1 < nkv) land(vf, (j + 1) * BN);
     __syncthreads();
   };
@@ -487,7 +507,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   static_assert(2 * 32 * OPITCH <= T::VBYTES, "two waves' rows of O fit in one V buffer");
   char* ob = (w < 2 ? vb0 : vb1) + (w & 1) * 32 * OPITCH;
   const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / (BF16 ? halves_sum(l_run - e_run) : l_tot);
 #pragma unroll
   for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll

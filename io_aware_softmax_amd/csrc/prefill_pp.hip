@@ -289,6 +289,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // lane's part of the denominator s, both relative to that reference.
   float m_ref = -INFINITY;
   float l_run = 0.f;
+  // bf16: sum over tiles of the rounding error (fp32 weight minus its bf16
+  // value) of this lane's largest weight of the tile.  The value product
+  // takes the rounded weights, so O is divided by l_run - e_run: the row's
+  // dominant weight then enters numerator and denominator with the same
+  // rounding and O stays a convex combination of the value rows (with the
+  // unrounded sum alone, a dominant weight off by up to 2^-8 relative moves
+  // O by that much of |v|).  LSE keeps the unrounded sum.
+  float e_run = 0.f;
   f32x16 sc[2];  // scores of the tile between the matrix and softmax phases
   s16x8 pb[4];   // weights of the tile between the softmax and matrix phases
 #pragma unroll
@@ -391,12 +399,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // reference advanced and the weights recomputed; the scores are still in
   // sc.  A tile this wave does not compute gets zero weights.
   auto softmax_tile = [&](int t) __attribute__((always_inline)) {
-    if (t >= w_nkv) {
+    // The common path falls through: the branches below are rarely taken
+    // (a taken branch stalls this wave's vector issue while the other
+    // wave's products run).
+    if (__builtin_expect(t >= w_nkv, 0)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) pb[i] = s16x8{};
       return;
     }
-    if (t >= j_mask) {
+    if (__builtin_expect(t >= j_mask, 0)) {
       // Per-lane key offset and query made opaque here, so the per-element
       // bounds are not hoisted out of the tile loop (registers).
       int hk = 8 * h, q = qi;
@@ -411,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
           if (!ok) sc[blk][r] = -INFINITY;
         }
     }
-    float psum = weights();
-    if (__any(!(psum <= kTauWeight) || m_ref == -INFINITY)) {
+    // This lane's largest score of the tile (keys excluded above are -inf).
+    auto lane_max = [&]() __attribute__((always_inline)) -> float {
       float mx = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -421,7 +432,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
           mx = fmaxf(mx, sc[blk][r]);
           mx = fmaxf(mx, sc[blk][r + 1]);
         }
-      mx = halves_max(mx);
+      return mx;
+    };
+    // bf16: rounding error of the lane's largest weight, recomputed from its
+    // largest score with the same arithmetic as weights() (bit-identical).
+    auto round_error = [&](float mx) __attribute__((always_inline)) -> float {
+      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      const float wmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, neg_m));
+      return wmax - __builtin_bit_cast(float, (unsigned)round16<true>(wmax) << 16);
+    };
+    float mx_lane = BF16 ? lane_max() : 0.f;
+    float psum = weights();
+    float e_t = BF16 ? round_error(mx_lane) : 0.f;
+    // The packed weights are complete before the check below, so the check
+    // is the last thing of the phase on the common path.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
+    if (__builtin_expect(__any(!(psum <= kTauWeight) || m_ref == -INFINITY), 0)) {
+      if constexpr (!BF16) mx_lane = lane_max();
+      const float mx = halves_max(mx_lane);
       // The guide's running maximum d_k = max(d_{k-1}, max of chunk k)
       // with headroom: a row whose tile maximum passed its reference moves
       // the reference kHeadroom above that maximum and corrects O~ and s by
@@ -433,11 +462,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
       m_ref = m_new;
       l_run *= alpha;
+      if constexpr (BF16) e_run *= alpha;
 #pragma unroll
       for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
       psum = weights();
+      if constexpr (BF16) e_t = round_error(mx_lane);
     }
     l_run += psum;
+    if constexpr (BF16) e_run += e_t;
   };
 
   // First tiles of an item (K_0, V_0, K_1), by group 0.
@@ -460,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
     m_ref = -INFINITY;
     l_run = 0.f;
+    e_run = 0.f;
     barrier_lds();  // the item's first tiles have landed
 
     // ---- the two groups' schedules, as separate loops (each wave executes
@@ -516,7 +549,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       // ---- epilogue of a key range: normalised partial O and its
       //      log-sum-exp (-inf, with O = 0, for a row with no key in it) ----
       const float l_tot = halves_sum(l_run);
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float l_o = BF16 ? halves_sum(l_run - e_run) : l_tot;
+      const float inv = l_tot > 0.f ? 1.f / l_o : 0.f;
       if (qi < Lq) {
         const size_t prow_ix = ((size_t)sp_s * BH + bh) * Lq + qi;
         float* po = part_o + prow_ix * D;
@@ -544,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     // and Q are loaded meanwhile (all tile reads of this item are done).
     char* ob = smem + LY::OST + w * 32 * LY::OPITCH;
     const float l_tot = halves_sum(l_run);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / (BF16 ? halves_sum(l_run - e_run) : l_tot);
 #pragma unroll
     for (int db = 0; db < T::DBLK; ++db)
 #pragma unroll
