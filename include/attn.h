@@ -66,7 +66,8 @@ typedef enum {
   ATTN_ERR_ALIGN = -9,          /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_HIP = -10,           /* a HIP launch or allocation failed */
   ATTN_ERR_MASK = -11,          /* bad mask_kind, or mask_b / mask_h not 1 or B / H */
-  ATTN_ERR_DROPOUT = -12        /* dropout_p outside [0, 1) */
+  ATTN_ERR_DROPOUT = -12,       /* dropout_p outside [0, 1) */
+  ATTN_ERR_WORKSPACE = -13      /* attn_decode_fwd_noalloc: partials exceed ATTN_NOALLOC_SCRATCH_BYTES */
 } attn_status_t;
 
 /* Kinds of the general mask of attn_fwd_ex / attn_bwd_ex. */
@@ -78,6 +79,9 @@ typedef enum {
 
 /* Largest split count accepted by attn_decode_fwd and attn_decode_varlen_fwd. */
 #define ATTN_MAX_SPLITS 256
+
+/* Bytes of the fixed device scratch of attn_decode_fwd_noalloc (16 MiB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * attn_fwd - attention forward for any supported shape.
@@ -128,6 +132,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int H, int Lk, int D, float scale, int num_splits,
                     void* stream, int dtype);
+
+/*
+ * attn_decode_fwd_noalloc - attn_decode_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation).
+ *
+ * Arguments, results and kernels are those of attn_decode_fwd (the same
+ * num_splits gives bit-identical o and lse), but the split partials,
+ * (D + 2) * 4 * B * H * splits bytes, live in a fixed device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends; the call makes no allocation of any
+ * kind.  Its device address is looked up on the first call per device.
+ * Returns ATTN_ERR_WORKSPACE (before any HIP call) when the partials
+ * would exceed ATTN_NOALLOC_SCRATCH_BYTES (B * H * splits <= 32263 at
+ * D = 128, <= 63550 at D = 64).  All calls on one device share that array:
+ * calls that overlap on one device (different streams, or host threads
+ * without ordering between them) race and give undefined results; calls
+ * ordered on one stream are safe.  Nothing in the array needs clearing:
+ * every call writes all partials it reads.
+ */
+int attn_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Lk, int D, float scale, int num_splits,
+                            void* stream, int dtype);
 
 /*
  * attn_decode_varlen_fwd - single-query attention over a KV cache whose

@@ -21,8 +21,9 @@ LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 _DTYPE_CODES = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
-EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_varlen_fwd", "attn_bwd", "attn_fwd_ex", "attn_bwd_ex",
+EXPORTED = ("attn_fwd", "attn_decode_fwd", "attn_decode_fwd_noalloc", "attn_decode_varlen_fwd", "attn_bwd", "attn_fwd_ex", "attn_bwd_ex",
             "attn_decode_auto_splits", "attn_prefill_split_plan", "attn_strerror")
 ATTN_MASK_NONE, ATTN_MASK_BOOL, ATTN_MASK_ADD = 0, 1, 2
 
@@ -57,6 +58,8 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
         lib.attn_decode_fwd.restype = i
+        lib.attn_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
+        lib.attn_decode_fwd_noalloc.restype = i
         lib.attn_decode_varlen_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
         lib.attn_decode_varlen_fwd.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, i]
@@ -239,6 +242,31 @@ def attn_decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Op
     _check(lib.attn_decode_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), B, H, Lk, D, scale, int(num_splits),
                                _stream_handle(stream), _DTYPE_CODES[q.dtype]))
+    return out, lse
+
+
+def attn_decode_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                            lse: torch.Tensor, scale: Optional[float] = None, num_splits: int = 0,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """``attn_decode_fwd_noalloc``: the split-KV decode with its partials in
+    the library's fixed device scratch (no allocation in the library).
+
+    The caller passes ``out`` [B,H,1,D] and ``lse`` [B,H,1] (nothing is
+    allocated here either).  Same results as ``attn_decode_fwd`` with the
+    same ``num_splits``.
+    """
+    lib = load()
+    B, H, Lq, D = _dims(q)
+    if Lq != 1:
+        raise ValueError("attn_decode_fwd_noalloc takes one query per (batch, head)")
+    if out is None or lse is None:
+        raise ValueError("out and lse are required (this entry point allocates nothing)")
+    Lk = _keys(k)
+    out, lse = _prep(q, k, v, out, lse, 1)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.attn_decode_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, Lk, D, scale, int(num_splits),
+                                       _stream_handle(stream), _DTYPE_CODES[q.dtype]))
     return out, lse
 
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_internal.hpp"
@@ -97,17 +98,17 @@ int auto_splits(int64_t BH, int Lk) {
   return int(s);
 }
 
-int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int Lk, int D, float scale, int splits, hipStream_t stream, int dtype,
-               const int* seqlens = nullptr) {
-  const int64_t BH = int64_t(B) * H;
-  if (splits == 0) splits = auto_splits(BH, Lk);
-  if (BH * splits > kMaxWorkgroups) return ATTN_ERR_DIM;
+// Bytes of split partials a decode call needs: [BH * splits] rows of D
+// floats (the normalised partial outputs), then the maxima and the sums.
+size_t decode_workspace_bytes(int64_t BH, int splits, int D) {
+  return size_t(BH) * splits * (size_t(D) + 2) * sizeof(float);
+}
+
+// The decode kernels on a given workspace of decode_workspace_bytes().
+hipError_t launch_decode_on(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                            int H, int Lk, int D, float scale, int splits, hipStream_t stream, int dtype,
+                            const int* seqlens, void* ws) {
   const size_t nparts = size_t(BH) * splits;
-  const size_t bytes = nparts * (size_t(D) + 2) * sizeof(float);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e);
   attn::DecodeArgs a;
   a.q = q;
   a.k = k;
@@ -125,11 +126,54 @@ int run_decode(const void* q, const void* k, const void* v, void* o, float* lse,
   a.keys_per_split = int((int64_t(Lk) + splits - 1) / splits);
   a.c = std::fabs(scale) * attn::kLog2e;
   a.neg = scale < 0.f;
-  e = attn::launch_decode(dtype, D, a, stream);
+  return attn::launch_decode(dtype, D, a, stream);
+}
+
+int run_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Lk, int D, float scale, int splits, hipStream_t stream, int dtype,
+               const int* seqlens = nullptr) {
+  const int64_t BH = int64_t(B) * H;
+  if (splits == 0) splits = auto_splits(BH, Lk);
+  if (BH * splits > kMaxWorkgroups) return ATTN_ERR_DIM;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, decode_workspace_bytes(BH, splits, D), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_decode_on(q, k, v, o, lse, BH, H, Lk, D, scale, splits, stream, dtype, seqlens, ws);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (ef != hipSuccess) return hip_fail(ef);
   return ATTN_OK;
+}
+
+// Scratch of attn_decode_fwd_noalloc: the split partials live in this
+// fixed device array instead of a stream-ordered allocation.  Every device
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is only a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address is passed to kernels.
+__device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the
+// first call per device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 // Checks and packs the mask / dropout arguments shared by attn_fwd_ex and
@@ -288,6 +332,24 @@ ATTN_EXPORT int attn_decode_fwd(const void* q, const void* k, const void* v, voi
                     dtype);
 }
 
+ATTN_EXPORT int attn_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        int B, int H, int Lk, int D, float scale, int num_splits,
+                                        void* stream, int dtype) {
+  const int st = validate(q, k, v, o, lse, B, H, 1, Lk, D, 0, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+  const int64_t BH = int64_t(B) * H;
+  const int splits = num_splits == 0 ? auto_splits(BH, Lk) : num_splits;
+  if (BH * splits > kMaxWorkgroups) return ATTN_ERR_DIM;
+  if (decode_workspace_bytes(BH, splits, D) > size_t(ATTN_NOALLOC_SCRATCH_BYTES)) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_decode_on(q, k, v, o, lse, BH, H, Lk, D, scale, splits, static_cast<hipStream_t>(stream), dtype,
+                       nullptr, ws);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 ATTN_EXPORT int attn_decode_varlen_fwd(const void* q, const void* k, const void* v, void* o,
                                        float* lse, const int* seqlens, int B, int H, int Lk_max,
                                        int D, float scale, int num_splits, void* stream,
@@ -402,6 +464,8 @@ ATTN_EXPORT const char* attn_strerror(int status) {
     case ATTN_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_ERR_MASK: return "mask_kind is not an attn_mask_kind_t, or mask_b / mask_h is not 1 or B / H";
     case ATTN_ERR_DROPOUT: return "dropout_p must be in [0, 1)";
+    case ATTN_ERR_WORKSPACE:
+      return "the call needs more than ATTN_NOALLOC_SCRATCH_BYTES of split partials (fewer splits or a smaller batch)";
     case ATTN_ERR_HIP:
       std::snprintf(g_status_msg, sizeof(g_status_msg), "HIP error: %s", g_hip_msg);
       return g_status_msg;

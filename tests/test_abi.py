@@ -48,6 +48,27 @@ def test_exports_every_declared_function(lib):
     assert exported == set(declared)
 
 
+def test_noalloc_validation_errors(lib):
+    """attn_decode_fwd_noalloc: the forward's checks, the split range, and
+    ATTN_ERR_WORKSPACE when the partials would not fit the fixed scratch,
+    all before any HIP call."""
+    e = {n: _header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_DIM", "ATTN_ERR_SPLITS", "ATTN_ERR_WORKSPACE",
+                                       "ATTN_ERR_ALIAS", "ATTN_ERR_UNSUPPORTED_D")}
+    n = lib.attn_decode_fwd_noalloc
+    cap = int(re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", HEADER.read_text()).group(1)) << 20
+    assert cap == binding.ATTN_NOALLOC_SCRATCH_BYTES
+    assert n(0, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, 4, None, 2) == e["ATTN_ERR_NULL"]
+    assert n(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 64, 0.1, 257, None, 2) == e["ATTN_ERR_SPLITS"]
+    assert n(G, 2 * G, 3 * G, 4 * G, 5 * G, 2, 3, 100, 48, 0.1, 4, None, 2) == e["ATTN_ERR_UNSUPPORTED_D"]
+    assert n(G, 2 * G, 3 * G, G, 5 * G, 2, 3, 100, 64, 0.1, 4, None, 2) == e["ATTN_ERR_ALIAS"]
+    # partials of (D + 2) * 4 bytes per (b, h, split): the largest B * H * splits that fits, and one more
+    for D in (64, 128):
+        fit = cap // ((D + 2) * 4)
+        H = fit // 256  # with 256 splits
+        assert n(G, 2 * G, 3 * G, 4 * G, 5 * G, 1, H + 1, 1 << 16, D, 0.1, 256, None, 2) == e["ATTN_ERR_WORKSPACE"]
+    assert n(G, 2 * G, 3 * G, 4 * G, 5 * G, 16, 32, 32768, 128, 0.1, 256, None, 2) == e["ATTN_ERR_WORKSPACE"]
+
+
 def test_header_constants_match_binding():
     assert _header_enum("ATTN_F32") == binding.ATTN_F32
     assert _header_enum("ATTN_F16") == binding.ATTN_F16
@@ -161,10 +182,10 @@ def test_ex_validation_errors(lib):
 
 
 def test_strerror_and_auto_splits(lib):
-    for code in range(-12, 1):
+    for code in range(-13, 1):
         msg = binding.attn_strerror(code)
         assert msg and msg != "unknown status"
-    assert binding.attn_strerror(-13) == "unknown status"
+    assert binding.attn_strerror(-14) == "unknown status"
     assert binding.attn_strerror(-10).startswith("HIP error")
     s = binding.attn_decode_auto_splits(16, 32, 32768, 128)
     assert 1 <= s <= binding.ATTN_MAX_SPLITS
