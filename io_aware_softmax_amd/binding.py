@@ -17,7 +17,9 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = Path(__file__).resolve().parent / "libattn.so"
+# IO_AWARE_SOFTMAX_LIB names another build of the same library (the CPU
+# tests run the host-sanitized build this way); by default the in-tree one.
+LIB_PATH = Path(os.environ.get("IO_AWARE_SOFTMAX_LIB") or (Path(__file__).resolve().parent / "libattn.so"))
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_MAX_SPLITS = 256

@@ -3,6 +3,8 @@
 Usage: ``python -m io_aware_softmax_amd.build`` or ``build()`` from Python.
 Objects go to ``_build/`` at the repository root; the library is written to
 ``io_aware_softmax_amd/libattn.so`` (atomically replaced).
+``python -m io_aware_softmax_amd.build --sanitize`` builds the host-sanitized
+variant ``_build/sanitize/libattn_sanitize.so`` for the CPU tests instead.
 """
 
 from __future__ import annotations
@@ -38,27 +40,52 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False) -> Path:
-    out = ROOT / "_build"
-    out.mkdir(exist_ok=True)
+# Host-side sanitizers for the CPU test tier (argument validation, the
+# split planner, the status strings): AddressSanitizer and UBSan on the
+# host code only; the GPU code is built as usual.  Each -fsanitize= follows
+# -Xarch_host so that it never reaches the device compilation.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_LIB = ROOT / "_build" / "sanitize" / "libattn_sanitize.so"
+
+
+def asan_runtime() -> Path:
+    """The shared AddressSanitizer runtime of the ROCm LLVM toolchain (to be
+    preloaded into a process that loads the sanitized library)."""
+    hits = sorted(Path("/opt/rocm/llvm/lib/clang").glob("*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm/lib/clang")
+    return hits[-1]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> Path:
+    """Compile every source and link the library.  sanitize=True builds the
+    host-sanitized variant SANITIZE_LIB instead (CPU tests only)."""
+    out = ROOT / "_build" / ("sanitize" if sanitize else "")
+    out.mkdir(parents=True, exist_ok=True)
+    flags = FLAGS + (SANITIZE_FLAGS if sanitize else [])
     jobs = []
     for src in SOURCES:
         obj = out / (Path(src).stem + ".o")
-        jobs.append((obj, [HIPCC, *FLAGS, "-c", str(PKG / "csrc" / src), "-o", str(obj)]))
+        jobs.append((obj, [HIPCC, *flags, "-c", str(PKG / "csrc" / src), "-o", str(obj)]))
     with ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 1)) as ex:
         msgs = list(ex.map(lambda j: _run(j[1]), jobs))
     if verbose:
         for m in msgs:
             if m.strip():
                 print(m, file=sys.stderr)
-    tmp = LIB.with_suffix(".so.tmp")
+    lib = SANITIZE_LIB if sanitize else LIB
+    tmp = lib.with_suffix(".so.tmp")
     # --no-undefined: a kernel whose host stub was not emitted must fail the
-    # build, not the first launch.
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-Wl,--no-undefined", "-o", str(tmp),
+    # build, not the first launch.  The sanitized variant links the shared
+    # sanitizer runtime, which the test process preloads.
+    link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"] \
+        if sanitize else []
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-Wl,--no-undefined", *link, "-o", str(tmp),
           *[str(o) for o, _ in jobs]])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))
