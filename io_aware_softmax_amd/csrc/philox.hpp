@@ -31,10 +31,12 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, PhiloxKey key) {
       k1 += W1;
     }
     // Full 64-bit products: one v_mad_u64_u32 each instead of a
-    // v_mul_hi_u32 / v_mul_lo_u32 pair.
+    // v_mul_hi_u32 / v_mul_lo_u32 pair; each three-way XOR is one
+    // v_bitop3_b32 (truth table 0x96) instead of two v_xor_b32.
     const uint64_t p0 = (uint64_t)M0 * x.x;
     const uint64_t p1 = (uint64_t)M1 * x.z;
-    x = make_uint4((unsigned)(p1 >> 32) ^ x.y ^ k0, (unsigned)p1, (unsigned)(p0 >> 32) ^ x.w ^ k1, (unsigned)p0);
+    x = make_uint4(__builtin_amdgcn_bitop3_b32((unsigned)(p1 >> 32), x.y, k0, 0x96), (unsigned)p1,
+                   __builtin_amdgcn_bitop3_b32((unsigned)(p0 >> 32), x.w, k1, 0x96), (unsigned)p0);
   }
   return x;
 }

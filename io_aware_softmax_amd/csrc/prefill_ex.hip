@@ -137,8 +137,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     for (int grp = 0; grp < 4; ++grp) asm volatile("" ::"v"(raw[grp].x), "v"(raw[grp].y));
   };
 
-  auto tile = [&](const char* stage, int kv0, const uint2 (&raw)[4]) __attribute__((always_inline)) {
-    if (kv0 >= w_key_end) return;
+  // Masks not loaded a tile ahead (additive: 128 bytes per lane and tile;
+  // boolean with dropout: no registers to spare): the tile loads its own
+  // terms and the next tile's K/V DMA is issued only after those terms have
+  // been added to the scores.  Any wait for the mask loads is a full vmcnt
+  // wait (the compiler does not count the DMA, which is inline assembly), so
+  // with the DMA issued first it would also wait for the DMA.
+  constexpr bool LATE_DMA = KIND != 0 && !PREF;
+  auto tile = [&](const char* stage, int kv0, const uint2 (&raw)[4], auto&& issue_next)
+                  __attribute__((always_inline)) {
+    if (kv0 >= w_key_end) {
+      if constexpr (LATE_DMA) issue_next();
+      return;
+    }
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
     // Mask terms of the tile's 32 keys, loaded before the score products so
@@ -186,6 +197,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         else
           s[b][r] *= c;
       }
+    if constexpr (LATE_DMA) issue_next();
     // Keys past Lk (without a mask: only in the last tile) and, in tiles
     // that cross the wave's first diagonal, keys past the query's diagonal.
     if (KIND == 0 && !whole) {
@@ -255,8 +267,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     if constexpr (PREF) {
       if (j + 1 < nkt) raw_load((j + 1) * BQ, rawB);
     }
-    if (j + 1 < nkt) issue(j + 1, smem + STAGE);
-    tile(smem, j * BQ, rawA);
+    auto next_a = [&]() __attribute__((always_inline)) {
+      if (j + 1 < nkt) issue(j + 1, smem + STAGE);
+    };
+    if constexpr (!LATE_DMA) next_a();
+    tile(smem, j * BQ, rawA, next_a);
     land_all();
     if constexpr (PREF) raw_landed(rawB);
     __syncthreads();
@@ -264,8 +279,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     if constexpr (PREF) {
       if (j + 2 < nkt) raw_load((j + 2) * BQ, rawA);
     }
-    if (j + 2 < nkt) issue(j + 2, smem);
-    tile(smem + STAGE, (j + 1) * BQ, rawB);
+    auto next_b = [&]() __attribute__((always_inline)) {
+      if (j + 2 < nkt) issue(j + 2, smem);
+    };
+    if constexpr (!LATE_DMA) next_b();
+    tile(smem + STAGE, (j + 1) * BQ, rawB, next_b);
     land_all();
     if constexpr (PREF) raw_landed(rawA);
     __syncthreads();
