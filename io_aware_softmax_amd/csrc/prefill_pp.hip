@@ -511,15 +511,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
       const int j_spread = max(0, min(nkv - 2, Lk / BN - 2 - (SPLIT ? jl_s : 0)));
       int j = 0;
-      for (; j < j_spread; ++j) {
+      auto spread_step = [&](int jj) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
-        matrix(j, IssueSpread{});
+        matrix(jj, IssueSpread{});
         barrier_lds();
         __builtin_amdgcn_s_setprio(0);
-        softmax_tile(j + 1);
-        land(vb(j + 1), (j + 1) * BN);
+        softmax_tile(jj + 1);
+        land(vb(jj + 1), (jj + 1) * BN);
         barrier_lds();
+      };
+      // Two steps per iteration: the buffer parity of each is then known at
+      // compile time and the tile offsets fold into the LDS read offsets.
+      for (; j + 1 < j_spread; j += 2) {
+        spread_step(j);
+        spread_step(j + 1);
       }
+      if (j < j_spread) spread_step(j++);
       for (; j < nkv; ++j) {
         __builtin_amdgcn_s_setprio(1);
         matrix(j, IssueUpfront{});
@@ -534,14 +541,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       __builtin_amdgcn_s_setprio(1);
       matrix_first();
       barrier_lds();
-      for (int j = 0; j < nkv; ++j) {
+      auto step = [&](int jj) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(0);
-        softmax_tile(j);
+        softmax_tile(jj);
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
-        matrix(j, NoIssue{});
+        matrix(jj, NoIssue{});
         barrier_lds();
+      };
+      int j = 0;
+      for (; j + 1 < nkv; j += 2) {  // two steps per iteration, as for group 0
+        step(j);
+        step(j + 1);
       }
+      if (j < nkv) step(j);
     }
     __builtin_amdgcn_s_setprio(0);
 
