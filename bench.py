@@ -16,7 +16,8 @@ duration) is reported under ``decode``; the backward of the prefill
 workload (dQ, dK, dV through ``attn_bwd``, timed on its own) under
 ``backward``.  ``cpu_baseline`` times the float64
 CPU oracle on a bounded sample of the prefill workload (test infrastructure,
-never part of the timed path).
+never part of the timed path); ``parity`` compares the timed prefill's
+output on those heads with the oracle's.
 """
 
 from __future__ import annotations
@@ -84,8 +85,36 @@ def _to_device(bits, dtype):
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
 
 
-def _cpu_baseline(wl, heads: int):
-    """Time the float64 oracle on the first ``heads`` heads (all rows)."""
+def _cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _round_to(x, dtype):
+    """float64 values rounded once, to nearest-even, to the output's storage
+    type (bf16 keeps 8 significant bits)."""
+    import numpy as np
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def _cpu_baseline(wl, heads: int, out=None, lse=None):
+    """Time the float64 oracle on the first ``heads`` heads (all rows).
+
+    With the device's output ``out`` [B, H, Lq, D] and ``lse`` [B, H, Lq]
+    also returns the parity of those heads against the oracle's result:
+    max|O - O_ref|, max|O - round(O_ref)| (the distance to the reference
+    rounded to the output type) and the largest relative LSE error."""
     import numpy as np
     import oracle
     from io_aware_softmax_amd import inputs
@@ -95,14 +124,29 @@ def _cpu_baseline(wl, heads: int):
     except Exception:
         threads = os.cpu_count() or 1
     slabs = [{t: inputs.slab_values(wl, t, 0, h)[None, None] for t in "qkv"} for h in range(heads)]
+    refs = []
     t0 = time.perf_counter()
     for s in slabs:
-        oracle.attention(s["q"], s["k"], s["v"], wl.scale, wl.causal)
+        refs.append(oracle.attention(s["q"], s["k"], s["v"], wl.scale, wl.causal))
     dt = time.perf_counter() - t0
     flops = wl.flops() * heads / (wl.B * wl.H)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"heads 0-{heads - 1} of {wl.H} (all {wl.Lq} rows) of the causal bf16 prefill, "
                       f"float64 NumPy, {dt:.1f} s for {flops:.3e} algorithmic flops"}
+    parity = None
+    if out is not None:
+        eo = er = el = 0.0
+        for h, (O_ref, L_ref) in enumerate(refs):
+            O = out[0, h].float().cpu().numpy().astype(np.float64)
+            L = lse[0, h].cpu().numpy().astype(np.float64)
+            O_ref, L_ref = O_ref[0, 0], L_ref[0, 0]
+            eo = max(eo, float(np.max(np.abs(O - O_ref))))
+            er = max(er, float(np.max(np.abs(O - _round_to(O_ref, wl.dtype)))))
+            el = max(el, float(np.max(np.abs(L - L_ref) / np.maximum(1.0, np.abs(L_ref)))))
+        parity = {"heads": f"0-{heads - 1} of {wl.H}, every row", "max_abs_O": eo,
+                  "max_abs_O_vs_rounded_ref": er, "max_rel_lse": el, "o_tol": 2e-2}
+    return base, parity
 
 
 def main():
@@ -277,7 +321,9 @@ def main():
                      "arch": getattr(props, "gcnArchName", "")}
     rec["input_gen_s"] = gen_s
     if run_p and not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _cpu_baseline(wp, args.cpu_heads)
+        # The timed loop's last prefill output is still in ``op``/``lp``
+        # (the backward leg rewrites them with the same values).
+        rec["cpu_baseline"], rec["parity"] = _cpu_baseline(wp, args.cpu_heads, op, lp)
     print(json.dumps(rec), flush=True)
 
 

@@ -5,7 +5,8 @@ Subcommands (run as ``python -m io_aware_softmax_amd.measure <cmd>``):
 * ``kernels`` - uploads the causal bf16 prefill (B1 H32 L8192 D128) and the
   bf16 decode (B16 H32 Lk32768 D128) inputs and runs each kernel call
   (prefill forward, its backward with a seeded upstream gradient, decode)
-  ``--reps`` times, for rocprofv3 kernel traces and counter passes.
+  ``--reps`` times, for rocprofv3 kernel traces and counter passes; with
+  ``--workload NAME`` only that workload's forward.
 * ``copy`` - copies a 1 GiB device buffer ``--reps`` times (torch's copy
   kernel): reads and writes exactly 2^30 bytes per launch, the reference
   that scales the FETCH_SIZE / WRITE_SIZE counters to bytes.
@@ -54,6 +55,19 @@ def _upload(wl):
 
 
 def cmd_kernels(args):
+    if args.workload:
+        # One forward workload on its own (e.g. the fp16 sweep's L = 4096
+        # point), for counter passes on the kernel that serves it.
+        wl = inputs.WORKLOADS[args.workload]
+        q, k, v = _upload(wl)
+        o = torch.empty_like(q)
+        lse = torch.empty(wl.B, wl.H, wl.Lq, dtype=torch.float32, device="cuda")
+        print(f"forward {wl.name}: {args.reps} launches", flush=True)
+        for _ in range(args.reps):
+            binding.attn_fwd(q, k, v, causal=wl.causal, scale=wl.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        print("done", flush=True)
+        return
     wp = inputs.WORKLOADS["causal_bf16_8k"]
     wd = inputs.WORKLOADS["decode_bf16_32k"]
     q, k, v = _upload(wp)
@@ -215,6 +229,7 @@ def main(argv=None):
     p.add_argument("cmd", choices=["kernels", "copy", "sweep", "sweep_ext", "ex"])
     p.add_argument("--reps", type=int, default=5)
     p.add_argument("--case", default="", help="ex: run only the case with this label")
+    p.add_argument("--workload", default="", help="kernels: run only this workload's forward")
     args = p.parse_args(argv)
     if not torch.cuda.is_available():
         print("needs a GPU", file=sys.stderr)
