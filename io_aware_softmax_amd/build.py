@@ -5,6 +5,8 @@ Objects go to ``_build/`` at the repository root; the library is written to
 ``io_aware_softmax_amd/libattn.so`` (atomically replaced).
 ``python -m io_aware_softmax_amd.build --sanitize`` builds the host-sanitized
 variant ``_build/sanitize/libattn_sanitize.so`` for the CPU tests instead.
+The measurement probe ``probes/gfx950_probe.hip`` (not part of the library)
+is built next to the objects as ``_build/gfx950_probe``.
 """
 
 from __future__ import annotations
@@ -84,7 +86,21 @@ def build(verbose: bool = False, sanitize: bool = False) -> Path:
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-Wl,--no-undefined", *link, "-o", str(tmp),
           *[str(o) for o, _ in jobs]])
     os.replace(tmp, lib)
+    if not sanitize:
+        build_probe()
     return lib
+
+
+PROBE = ROOT / "_build" / "gfx950_probe"
+
+
+def build_probe() -> Path:
+    """The stand-alone issue-cost / LDS-throughput probe executable."""
+    PROBE.parent.mkdir(parents=True, exist_ok=True)
+    tmp = PROBE.with_name(PROBE.name + ".tmp")
+    _run([HIPCC, *FLAGS, "-o", str(tmp), str(PKG / "probes" / "gfx950_probe.hip")])
+    os.replace(tmp, PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":

@@ -1,8 +1,9 @@
 // Reading a general attention mask and drawing dropout keep bits inside the
 // fused tile (the comfyai.app chapter "6.3 FlashAttention", section 6.3.3,
 // "Kernel Fusion": scores, scale, mask, softmax, dropout and the value
-// product in one kernel).  The mask kind is a run-time value (one kernel
-// serves boolean and additive masks); the branches on it are uniform.
+// product in one kernel).  The mask kind is a template argument: each kernel
+// is instantiated once per (mask kind, dropout), so a variant does only its
+// own per-element work.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,17 +69,6 @@ __device__ __forceinline__ void mask_terms8_kind(const MaskDropout& md, size_t i
       for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? v[e] * kLog2e : -INFINITY;
     }
   }
-}
-
-// The same with the kind read from md (a wave-uniform branch).
-__device__ __forceinline__ void mask_terms8(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
-                                            float (&t)[8]) {
-  if (md.kind == 0)
-    mask_terms8_kind<0>(md, idx, j0, Lk, vec, t);
-  else if (md.kind == 1)
-    mask_terms8_kind<1>(md, idx, j0, Lk, vec, t);
-  else
-    mask_terms8_kind<2>(md, idx, j0, Lk, vec, t);
 }
 
 }  // namespace attn
