@@ -28,6 +28,16 @@
 //     operand (P^T, 8 consecutive keys) of the P V product;
 //   * V stays row-major in LDS and is read transposed with ds_read_b64_tr_b16
 //     to form the A operand (V^T) of O^T += V^T P^T.
+//
+// Reference maximum: the guide's correction exp(d_old - d_new) gives the same
+// O and LSE for any reference d, so d moves only when needed.  fp16 computes
+// the weights against the current d and checks that no lane's weight sum
+// passes 2^8 (then no weight does, and the fp16 weights cannot overflow);
+// otherwise the tile's row maximum becomes d, O~ and s are corrected and the
+// weights recomputed (rare).  bf16 keeps a look-ahead: the row maximum of the
+// next tile is reduced while the current one's value product runs, d moves
+// before that tile's weights when it passes d + 8, and the same maximum
+// gives the rounding term of the largest weight (below).
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
@@ -61,7 +71,7 @@ constexpr float kTau = 8.f;
 // slot 0 so that the first K reads are in flight while the VALU works.
 constexpr int kDmaRun = 2;  // DMA instructions per M0 run
 
-template <int D>
+template <int D, bool LOOKAHEAD>
 struct Slots {
   using T = Tile<D>;
   using KP = DmaPlan<T::KINST, kDmaRun, NW>;
@@ -71,7 +81,10 @@ struct Slots {
   static constexpr int N = NS + NP;
   static constexpr int PF = 4;               // read lookahead, in slots (even)
   static constexpr int F = 6;                // softmax elements before slot 0
-  static constexpr int NV = NS + 2 * T::DBLK;  // slots the other elements spread over
+  // Slots the other elements spread over: with the look-ahead maximum the
+  // weights may run into the first value products of their k-step; with the
+  // weight-sum check every weight is done before the first value product.
+  static constexpr int NV = LOOKAHEAD ? NS + 2 * T::DBLK : NS;
   static constexpr int NR = KP::RUNS + VP::RUNS;  // DMA runs per step (K first)
   // Slot of softmax element e >= F, of max step m (values 2m, 2m+1), of DMA run q.
   static constexpr int elem_slot(int e) { return (e - F) * NV / (32 - F); }
@@ -84,18 +97,64 @@ struct Slots {
     return true;
   }
   static_assert(deadlines_met(), "softmax element scheduled after its value product");
+  static_assert(LOOKAHEAD || elem_slot(31) < NS, "weights must be done before the check");
   static_assert(PF % 2 == 0 && NS % 2 == 0 && NP % 2 == 0, "operand pairs");
   static_assert(max_slot(15) < N && dma_slot(NR - 1) < N, "slot overflow");
 };
 
+// The weight-sum check failed for some row of the wave (fp16): the tile's
+// row maximum (base-2 scaled units) becomes the reference where it is above
+// the old one, O~ and the lane's sum s take the guide's correction
+// exp(d_old - d_new), and the weights of the tile are recomputed (now all at
+// most 1).  `live` gives the unmasked keys when MASK.
+template <bool BF16, int D, bool MASK>
+__device__ __forceinline__ void move_reference(const f32x16 (&s)[2], s16x8 (&pb)[4], f32x16 (&oacc)[D / 32],
+                                                         float c, unsigned live, float& m_ref, float& l_run,
+                                                         float& psum) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+  mx = halves_max(mx);
+  const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
+  const bool grow = m_tile > m_ref;
+  const float m_new = grow ? m_tile : m_ref;
+  const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+  m_ref = m_new;
+  l_run *= alpha;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  psum = 0.f;
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int blk = st >> 1, r = 8 * (st & 1) + e;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_use));
+      if constexpr (MASK) p = ((live >> (16 * blk + r)) & 1u) ? p : 0.f;
+      pb[st][e] = (short)round16<BF16>(p);
+      psum += p;
+    }
+}
+
+// Weight-sum check: false when every weight of every row of the wave is at
+// most 2^kTau and every row has a reference (a NaN sum fails too).
+__device__ __forceinline__ bool weights_bounded(float psum, float m_ref) {
+  constexpr float kSumMax = 256.f;  // 2^kTau
+  return !__builtin_expect(__any(!(psum <= kSumMax) || m_ref == -INFINITY), 0);
+}
+
 template <bool BF16, int D>
 __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const s16x8 (&qreg)[D / 16],
                                           const f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&oacc)[D / 32],
-                                          float c, float neg_m, float& psum_out, float& mx_out,
+                                          float c, float& m_ref, float& l_run, float& mx_out,
                                           const char* kgbase, char* kdst, const unsigned* k_off,
                                           const char* vgbase, char* vdst, const unsigned* v_off, int w) {
+  constexpr bool LOOKAHEAD = BF16;
   using T = Tile<D>;
-  using S = Slots<D>;
+  using S = Slots<D, LOOKAHEAD>;
   using KP = typename S::KP;
   using VP = typename S::VP;
   if constexpr (VP::X != 0) {
@@ -108,6 +167,7 @@ __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const 
   s16x8 pb[4];
   float psum = 0.f;
   float mx = -INFINITY;
+  const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
   auto read = [&](int r) {
     if (r < S::NS) {
       fr[r] = *reinterpret_cast<const s16x8*>(kp + 32 * (r & 1) * T::KPITCH + 32 * (r >> 1));
@@ -160,15 +220,25 @@ __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const 
 #pragma unroll
     for (int e = S::F; e < 32; ++e)
       if (S::elem_slot(e) == i) elem(e);
+    if constexpr (LOOKAHEAD) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-      if (S::max_slot(m) == i) {
-        mx = fmaxf(mx, sn[m >> 3][2 * (m & 7)]);
-        mx = fmaxf(mx, sn[m >> 3][2 * (m & 7) + 1]);
-      }
+      for (int m = 0; m < 16; ++m)
+        if (S::max_slot(m) == i) {
+          mx = fmaxf(mx, sn[m >> 3][2 * (m & 7)]);
+          mx = fmaxf(mx, sn[m >> 3][2 * (m & 7) + 1]);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LOOKAHEAD) {
+      // Every weight of the tile is done: check them before the first value
+      // product uses them.
+      if (i == S::NS - 1) {
+        if (!weights_bounded(psum, m_ref)) move_reference<BF16, D, false>(sc, pb, oacc, c, 0u, m_ref, l_run, psum);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
-  psum_out = psum;
+  l_run += psum;
   mx_out = mx;
 }
 
@@ -237,8 +307,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
   // DMA of one K or V tile (DmaPlan); rows past Lk read row Lk-1 and the V
   // slots of those rows are zeroed once the DMA has landed.  Offsets are
   // biased for dma_run.
-  using KP = typename Slots<D>::KP;
-  using VP = typename Slots<D>::VP;
+  using KP = typename Slots<D, BF16>::KP;
+  using VP = typename Slots<D, BF16>::VP;
   unsigned k_src[KP::N];
   unsigned v_src[VP::N];
 #pragma unroll
@@ -389,6 +459,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
         psum += p;
       }
     }
+    if constexpr (!BF16) {
+      if (!weights_bounded(psum, m_ref)) move_reference<BF16, D, MASK>(s, pb, oacc, c, live, m_ref, l_run, psum);
+    }
     l_run += psum;
   };
   // O^T += V^T P^T; V^T fragments via transposed LDS reads.
@@ -451,15 +524,15 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
     s16x8 pb[4];
     float m_next = -INFINITY;
     if constexpr (FAST) {
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      float psum, mx;
+      float mx;
       fast_step<BF16, D>(kn + prow * T::KPITCH + 16 * h,
                          vc + (8 * h + (li >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (li & 3)) * 2, qreg, sc,
-                         sn, oacc, c, -m_use, psum, mx, biased(Kb + (size_t)(j + 2) * BN * (D * 2)), kf, k_src,
+                         sn, oacc, c, m_ref, l_run, mx, biased(Kb + (size_t)(j + 2) * BN * (D * 2)), kf, k_src,
                          biased(Vb + (size_t)(j + 1) * BN * (D * 2)), vf, v_src, w);
-      l_run += psum;
-      mx = halves_max(mx);
-      m_next = (mx == -INFINITY) ? -INFINITY : mx * c;
+      if constexpr (BF16) {
+        mx = halves_max(mx);
+        m_next = (mx == -INFINITY) ? -INFINITY : mx * c;
+      }
     } else {
       // Fences between the phases keep the operand reads of one phase from
       // being hoisted into the previous one (register pressure).
@@ -471,12 +544,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
       __builtin_amdgcn_sched_barrier(0);
       if (do_next) {
         live_n = mask_scores(sn, (j + 1) * BN);
-        m_next = row_max(sn);
+        if constexpr (BF16) m_next = row_max(sn);
       }
     }
-    if (do_cur) add_round_error(m_cur, (m_ref == -INFINITY) ? 0.f : m_ref);
-    if (do_next) advance_max(m_next);
-    m_cur = do_next ? m_next : -INFINITY;
+    if constexpr (BF16) {
+      if (do_cur) add_round_error(m_cur, (m_ref == -INFINITY) ? 0.f : m_ref);
+      if (do_next) advance_max(m_next);
+      m_cur = do_next ? m_next : -INFINITY;
+    }
     if (j + 1 < nkv) land(vf, (j + 1) * BN);
     __syncthreads();
   };

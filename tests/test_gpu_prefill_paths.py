@@ -180,3 +180,30 @@ def test_two_group_d64_reference_paths(dtype, monkeypatch):
     vals = {t: _normal((1, 2, 400, D), 710 + i) for i, t in enumerate("qkv")}
     for causal in (False, True):
         _check(f"huge D64 {dtype} c{int(causal)}", vals, dtype, causal, 40.0)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_group_reference_paths(dtype, D, monkeypatch):
+    """The single-group kernel (the default at D = 64; ATTN_PREFILL_KERNEL=single
+    at D = 128): row maxima that rise tile after tile (fp16: the weight-sum
+    check fails and the tile is redone from its maximum; bf16: the
+    look-ahead maximum moves the reference), that fall (only the first tile
+    sets it), and scale 40 (weights overflow to inf)."""
+    B, H, L = 1, 2, 1500
+    if D == 128:
+        monkeypatch.setenv("ATTN_PREFILL_KERNEL", "single")
+    say(f"case single-group reference paths D{D} {dtype}")
+    for pattern in ("rising", "falling"):
+        q = 0.1 * _normal((B, H, L, D), 621 + D)
+        k = 0.1 * _normal((B, H, L, D), 622 + D)
+        v = _normal((B, H, L, D), 623 + D)
+        q[..., 0] = 1.0
+        ramp = np.arange(L, dtype=np.float32) * 0.3
+        k[..., 0] = ramp if pattern == "rising" else ramp[::-1]
+        for causal in (False, True):
+            _check(f"single {pattern} D{D} {dtype} c{int(causal)}", {"q": q, "k": k, "v": v}, dtype, causal,
+                   1.0 / np.sqrt(D))
+    vals = {t: _normal((1, 2, 400, D), 720 + i + D) for i, t in enumerate("qkv")}
+    for causal in (False, True):
+        _check(f"single huge D{D} {dtype} c{int(causal)}", vals, dtype, causal, 40.0)
