@@ -103,10 +103,18 @@ def cmd_copy(args):
     print("done", flush=True)
 
 
-def _time(fn, reps, warmup=3):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+def _time(fn, reps, warm_s=0.2):
+    """Median and minimum event time of ``reps`` calls, after at least
+    ``warm_s`` seconds of back-to-back calls: the shader clock needs tens of
+    milliseconds of load to settle, and a few warm-up calls would time the
+    ramp instead of the steady state."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record()
