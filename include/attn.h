@@ -221,10 +221,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  *     aligned, of kind ATTN_MASK_BOOL (uint8) or ATTN_MASK_ADD (float32
  *     added to scale * q.k); ignored (may be NULL) for ATTN_MASK_NONE.  It
  *     combines with causal: a key is excluded if either excludes it.
- *   - dropout_p in [0, 1): each weight P_ij is kept iff word (j mod 4) of
- *     Philox4x32-10 (Salmon et al., SC 2011) with counter
- *     (j / 4, i, b * H + h, offset) and key (seed low 32 bits, seed high 32
- *     bits) is >= floor(dropout_p * 2^32); kept weights are scaled by
+ *   - dropout_p in [0, 1): each weight P_ij is kept iff the 16-bit half
+ *     (j mod 2; 0 = low half) of word ((j mod 8) / 2) of Philox4x32-10
+ *     (Salmon et al., SC 2011) with counter (j / 8, i, b * H + h, offset)
+ *     and key (seed low 32 bits, seed high 32 bits) is >=
+ *     floor(dropout_p * 2^16); kept weights are scaled by
  *     1 / (1 - dropout_p).  lse is computed from the weights before dropout.
  *     The same (seed, offset) gives the same pattern in attn_bwd_ex.
  * A row with no key left gets o = 0 and lse = -inf.  Shapes, lse and the

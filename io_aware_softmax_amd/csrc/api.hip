@@ -201,8 +201,8 @@ int make_mask_dropout(const void* mask, int mask_kind, int mask_b, int mask_h, f
     md->mask_h = mask_h;
   }
   md->dropout = dropout_p > 0.f;
-  const double thr = std::floor(double(dropout_p) * 4294967296.0);
-  md->thr = thr >= 4294967295.0 ? 0xFFFFFFFFu : unsigned(thr);
+  const double thr = std::floor(double(dropout_p) * 65536.0);
+  md->thr = (thr >= 65535.0 ? 0xFFFFu : unsigned(thr)) << 16;
   md->rp = float(1.0 / (1.0 - double(dropout_p)));
   md->k0 = unsigned(seed & 0xFFFFFFFFull);
   md->k1 = unsigned(seed >> 32);

@@ -68,7 +68,7 @@ struct MaskDropout {
   int mask_h;        // 1 (broadcast over heads) or H
   int H;             // heads: bh = b * H + h
   bool dropout;      // p > 0
-  unsigned thr;      // keep iff the Philox word is >= thr = floor(p 2^32)
+  unsigned thr;      // floor(p 2^16) << 16: a 16-bit Philox half h is kept iff (h << 16) >= thr
   float rp;          // 1 / (1 - p)
   unsigned k0, k1;   // Philox key: the seed's low and high words
   unsigned offset;   // Philox counter word 3

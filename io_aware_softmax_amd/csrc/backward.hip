@@ -372,40 +372,47 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
         for (int r = 0; r < 16; ++r) mt[r] = v[r] * kLog2e;
       }
     }
-    // Dropout keep bits of the 16 elements (bit r).  Element r needs word
-    // (key mod 4) of the Philox block of (key / 4, query of r); the 4 lanes of
-    // a quad hold keys 4m .. 4m+3 of one half-wave and need the same 16
-    // blocks.  Lane u of the quad computes the blocks of r = 4 t + u, and the
-    // quad exchanges words with DPP quad permutations: in rotation k, lane v
-    // offers word (v + k) mod 4 of its block and lane u takes it from lane
-    // (u - k) mod 4 -- word u of the block of r = 4 t + ((u - k) mod 4).
+    // Dropout keep bits of the 16 elements (bit r).  Element r needs the
+    // half (key mod 2) of word ((key mod 8) / 2) of the Philox block of
+    // (key / 8, query of r).  The 8 lanes n = 8m .. 8m + 7 of a half-wave hold
+    // the 8 keys of one block column and need the same 16 blocks.  Lane
+    // u = n mod 8 computes the blocks of r = u and r = 8 + u: each gives the
+    // keep bits of the 8 keys for one query, one byte (bit e: key 8m + e).
+    // The 8 lanes then transpose their two 8 x 8 bit matrices at once in three
+    // butterfly stages (k = 4, 2, 1): lanes u and u ^ k swap the k-bit
+    // groups that sit on the wrong side, after which lane u holds bit r = the
+    // keep bit of its own key for the query of r.  Lane exchanges are DPP
+    // moves (xor 1 and 2: quad permutations; xor 4: the half-row mirror,
+    // u -> 7 - u, then the quad permutation u -> u ^ 3); selections are bit
+    // masks (a lane-dependent ternary chain here becomes divergent branches).
     unsigned kbits = 0xFFFFu;
     if constexpr (DROP) {
-      kbits = 0u;
-      const int u = n & 3;
+      const unsigned u = (unsigned)n & 7u;
+      unsigned x = 0u;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * t + u;
-        const int qi = qb + 16 * (r >> 3) + 8 * h + (r & 7);
-        const uint4 wd = philox4x32_10(make_uint4((unsigned)key >> 2, (unsigned)qi, (unsigned)bh, md.offset), pk);
-        const unsigned wv[4] = {wd.x, wd.y, wd.z, wd.w};
-        static_for<4>([&](auto K) __attribute__((always_inline)) {
-          constexpr int k = decltype(K)::value;
-          // Word (u + k) mod 4 by bit masks: a lane-dependent ternary chain
-          // here becomes divergent branches.
-          const unsigned sel = (unsigned)(u + k);
-          const unsigned m0 = 0u - (sel & 1u), m1 = 0u - ((sel >> 1) & 1u);
-          const unsigned a01 = (wv[1] & m0) | (wv[0] & ~m0);
-          const unsigned a23 = (wv[3] & m0) | (wv[2] & ~m0);
-          const unsigned offer = (a23 & m1) | (a01 & ~m1);
-          // quad_perm control: lane u reads lane (u - k) mod 4
-          constexpr int kPerm = ((0 - k) & 3) | (((1 - k) & 3) << 2) | (((2 - k) & 3) << 4) | (((3 - k) & 3) << 6);
-          unsigned got = offer;
-          if constexpr (k != 0) got = (unsigned)__builtin_amdgcn_mov_dpp((int)offer, kPerm, 0xF, 0xF, false);
-          const int rr = 4 * t + ((u - k) & 3);
-          kbits |= (got >= md.thr ? 1u : 0u) << rr;
-        });
+      for (int t = 0; t < 2; ++t) {
+        const int qi = qb + 16 * t + 8 * h + (int)u;  // query of r = 8 t + u
+        const uint4 wd = philox4x32_10(make_uint4((unsigned)key >> 3, (unsigned)qi, (unsigned)bh, md.offset), pk);
+        x |= keep_bits8(wd, md.thr) << (8 * t);
       }
+      static_for<3>([&](auto S) __attribute__((always_inline)) {
+        constexpr int k = 4 >> decltype(S)::value;
+        constexpr unsigned lo = k == 4 ? 0x0F0Fu : (k == 2 ? 0x3333u : 0x5555u);
+        unsigned y;
+        if constexpr (k == 4) {
+          y = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+          y = (unsigned)__builtin_amdgcn_mov_dpp((int)y, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
+        } else if constexpr (k == 2) {
+          y = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        } else {
+          y = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        }
+        const unsigned a = (x & lo) | ((y & lo) << k);     // lanes with bit k of u clear
+        const unsigned b = (x & ~lo) | ((y >> k) & lo);    // lanes with bit k of u set
+        const unsigned m = 0u - ((u / k) & 1u);
+        x = (b & m) | (a & ~m);
+      });
+      kbits = x & 0xFFFFu;
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll

@@ -6,9 +6,12 @@
 // products), then outputs (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1,
 // lo(M0 x0)); the key is bumped by the Weyl constants between rounds.
 //
-// Dropout: the weight of (batch-head bh, query i, key j) is kept iff word
-// (j mod 4) of Philox4x32-10(counter = (j / 4, i, bh, offset),
-// key = (seed low, seed high)) is >= the threshold floor(p 2^32).
+// Dropout: the weight of (batch-head bh, query i, key j) is kept iff the
+// 16-bit half (j mod 2; 0 the low half) of word ((j mod 8) / 2) of
+// Philox4x32-10(counter = (j / 8, i, bh, offset), key = (seed low, seed
+// high)) is >= floor(p 2^16).  One block serves 8 consecutive keys.  The
+// threshold travels shifted: thr = floor(p 2^16) << 16, so a high half is
+// kept iff word >= thr and a low half iff (word << 16) >= thr.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,22 +44,18 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, PhiloxKey key) {
   return x;
 }
 
+// Keep bits of the 8 keys of one block: bit e is key 8 (block) + e.
+__device__ __forceinline__ unsigned keep_bits8(uint4 a, unsigned thr) {
+  return ((a.x << 16) >= thr ? 1u : 0u) | (a.x >= thr ? 2u : 0u) | ((a.y << 16) >= thr ? 4u : 0u) |
+         (a.y >= thr ? 8u : 0u) | ((a.z << 16) >= thr ? 16u : 0u) | (a.z >= thr ? 32u : 0u) |
+         ((a.w << 16) >= thr ? 64u : 0u) | (a.w >= thr ? 128u : 0u);
+}
+
 // Keep bits of keys j0 .. j0 + 7 (j0 a multiple of 8) for query i: bit e is
 // key j0 + e.
 __device__ __forceinline__ unsigned dropout_keep8(PhiloxKey key, unsigned j0, unsigned i, unsigned bh,
                                                   unsigned offset, unsigned thr) {
-  const uint4 a = philox4x32_10(make_uint4(j0 >> 2, i, bh, offset), key);
-  const uint4 b = philox4x32_10(make_uint4((j0 >> 2) + 1, i, bh, offset), key);
-  return (a.x >= thr ? 1u : 0u) | (a.y >= thr ? 2u : 0u) | (a.z >= thr ? 4u : 0u) | (a.w >= thr ? 8u : 0u) |
-         (b.x >= thr ? 16u : 0u) | (b.y >= thr ? 32u : 0u) | (b.z >= thr ? 64u : 0u) | (b.w >= thr ? 128u : 0u);
-}
-
-// Keep bit of one (query i, key j).
-__device__ __forceinline__ bool dropout_keep1(PhiloxKey key, unsigned j, unsigned i, unsigned bh, unsigned offset,
-                                              unsigned thr) {
-  const uint4 a = philox4x32_10(make_uint4(j >> 2, i, bh, offset), key);
-  const unsigned w = (j & 2) ? ((j & 1) ? a.w : a.z) : ((j & 1) ? a.y : a.x);
-  return w >= thr;
+  return keep_bits8(philox4x32_10(make_uint4(j0 >> 3, i, bh, offset), key), thr);
 }
 
 }  // namespace attn

@@ -21,14 +21,16 @@ the paper.
 
 Dropout reading (the comfyai.app chapter "6.3 FlashAttention" lists dropout
 between the softmax and the value product of the fused tile, section 6.3.3,
-"Kernel Fusion", without fixing a generator): the weight P_ij of
-(b, h, i, j) is kept iff word (j mod 4) of
+"Kernel Fusion", without fixing a generator or the width of the uniform):
+the weight P_ij of (b, h, i, j) is kept iff the 16-bit half (j mod 2: 0 the
+low half, 1 the high half) of word ((j mod 8) / 2) of
 
-    Philox4x32-10(counter = (j / 4, i, b H + h, offset),
+    Philox4x32-10(counter = (j / 8, i, b H + h, offset),
                   key = (seed mod 2^32, seed / 2^32))
 
-is >= floor(p 2^32), with p the float32 dropout probability; kept weights
-are scaled by 1 / (1 - p).
+is >= floor(p 2^16), with p the float32 dropout probability; kept weights
+are scaled by 1 / (1 - p).  One block thus serves 8 consecutive keys; the
+keep rate is 1 - floor(p 2^16) / 2^16, within 2^-16 of 1 - p.
 """
 
 from __future__ import annotations
@@ -84,19 +86,20 @@ def philox4x32(c0, c1, c2, c3, k0, k1, rounds=10):
 
 
 def dropout_threshold(p: float) -> int:
-    """floor(p 2^32) for the float32 value of p, p in [0, 1)."""
+    """floor(p 2^16) for the float32 value of p, p in [0, 1)."""
     p32 = float(np.float32(p))
     if not 0.0 <= p32 < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(math.floor(p32 * 4294967296.0)), 0xFFFFFFFF)
+    return min(int(math.floor(p32 * 65536.0)), 0xFFFF)
 
 
 def keep_pattern(seed: int, offset: int, bh: int, rows, Lk: int, p: float) -> np.ndarray:
     """Boolean [len(rows), Lk]: which weights of (b H + h = bh) survive dropout."""
     rows = np.asarray(rows, dtype=np.uint64)[:, None]
     j = np.arange(Lk, dtype=np.uint64)[None, :]
-    words = philox4x32(j >> np.uint64(2), rows, np.uint64(bh), np.uint64(offset & 0xFFFFFFFF),
+    words = philox4x32(j >> np.uint64(3), rows, np.uint64(bh), np.uint64(offset & 0xFFFFFFFF),
                        np.uint64(seed & 0xFFFFFFFF), np.uint64((seed >> 32) & 0xFFFFFFFF))
-    sel = (j & np.uint64(3)).astype(np.int64)
+    sel = ((j >> np.uint64(1)) & np.uint64(3)).astype(np.int64)
     w = np.choose(np.broadcast_to(sel, (rows.shape[0], Lk)), [np.broadcast_to(x, (rows.shape[0], Lk)) for x in words])
-    return w >= np.uint64(dropout_threshold(p))
+    half = (w >> (np.uint64(16) * (j & np.uint64(1)))) & np.uint64(0xFFFF)
+    return half >= np.uint64(dropout_threshold(p))

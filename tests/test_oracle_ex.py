@@ -65,19 +65,26 @@ def test_philox32_known_answers():
 
 
 def test_keep_pattern_reads_the_known_answer_words():
-    """keep_pattern takes word (j mod 4) of the block with counter
-    (j / 4, i, bh, offset) and key (seed low, seed high): with the all-zero
-    KAT counter and key (block 0 of row 0, bh 0, offset 0, seed 0) the four
-    keys see exactly that vector's four words."""
+    """keep_pattern takes, for key j, the 16-bit half (j mod 2; low half
+    first) of word ((j mod 8) / 2) of the block with counter
+    (j / 8, i, bh, offset) and key (seed low, seed high): with the all-zero
+    KAT counter and key (block 0 of row 0, bh 0, offset 0, seed 0) keys
+    0 .. 7 see exactly the halves of that vector's four words, in order."""
     words, expect = _kat_rows()[0]
     assert words == [0] * 6
-    for w in expect:
-        # p just above w / 2^32: words <= w are dropped, larger ones kept.
-        p = float(np.nextafter(np.float32(w / 2.0 ** 32), np.float32(1.0)))
+    halves = [h for w in expect for h in (w & 0xFFFF, w >> 16)]
+    assert len(halves) == 8
+    for x in halves:
+        # p just above x / 2^16: halves <= x are dropped, larger ones kept.
+        p = float(np.nextafter(np.float32((x + 0.5) / 2.0 ** 16), np.float32(1.0)))
         thr = ph.dropout_threshold(p)
-        assert thr > w
-        keep = ph.keep_pattern(0, 0, 0, [0], 4, p)[0]
-        assert list(keep) == [x >= thr for x in expect]
+        assert thr == x
+        keep = ph.keep_pattern(0, 0, 0, [0], 8, p)[0]
+        assert list(keep) == [y >= thr for y in halves]
+        assert keep[halves.index(x)]  # a half equal to the threshold is kept
+    # the eight thresholds keep eight different numbers of keys: every case
+    # tells the halves apart
+    assert len({sum(y >= x for y in halves) for x in halves}) == len(set(halves)) == 8
 
 
 @pytest.mark.parametrize("key", [(1, 2), (0, 0), (0xDEADBEEFCAFEF00D, 0x0123456789ABCDEF)])
@@ -150,7 +157,9 @@ def test_keep_pattern_properties():
              ph.keep_pattern(1, 0, 3, np.arange(100), 333, 0.3)]
     for o in other:
         assert (o != full).mean() > 0.3
-    assert ph.dropout_threshold(0.5) == 2 ** 31
+    assert ph.dropout_threshold(0.5) == 2 ** 15
+    assert ph.dropout_threshold(0.0) == 0
+    assert ph.dropout_threshold(float(np.nextafter(np.float32(1.0), np.float32(0.0)))) == 0xFFFF
     with pytest.raises(ValueError):
         ph.dropout_threshold(1.0)
 
