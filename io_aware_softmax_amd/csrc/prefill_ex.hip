@@ -144,11 +144,43 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   // wait (the compiler does not count the DMA, which is inline assembly), so
   // with the DMA issued first it would also wait for the DMA.
   constexpr bool LATE_DMA = KIND != 0 && !PREF;
+
+  // Additive masks without dropout: the 128 bytes of a lane's terms for the
+  // next tile are loaded once this tile's weights are done (its own terms
+  // are dead by then), after the next tile's K/V DMA.  The landing wait at
+  // the end of the tile then waits for the DMA but leaves those 8 loads in
+  // flight (vmcnt(8)); they are consumed after the next tile's score
+  // products, so their latency spans the value products, the barrier and
+  // the score products.
+  constexpr bool PREF_ADD = KIND == 2 && !DROP;
+  constexpr int kAmLoads = 8;  // global_load_dwordx4 per lane and tile
+  float4 am[kAmLoads];
+  const float* m32 = static_cast<const float*>(md.mask);
+  // Whole tiles of aligned rows take the loads (the in-tile path reads the rest).
+  auto am_vec = [&](int kv0) __attribute__((always_inline)) { return Lk % 8 == 0 && kv0 + BQ <= Lk; };
+  auto am_load = [&](int kv0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const size_t i0 = mrow + kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
+      am[2 * grp] = *reinterpret_cast<const float4*>(m32 + i0);
+      am[2 * grp + 1] = *reinterpret_cast<const float4*>(m32 + i0 + 4);
+    }
+  };
+  // End-of-tile landing: every DMA issued so far has landed; with `keep`,
+  // the last kAmLoads vector loads (issued after it) may still be in flight.
+  auto land = [&](bool keep) __attribute__((always_inline)) {
+    if (keep)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kAmLoads) : "memory");
+    else
+      land_all();
+  };
+
+  // Returns whether the next tile's mask terms were loaded (PREF_ADD).
   auto tile = [&](const char* stage, int kv0, const uint2 (&raw)[4], auto&& issue_next)
-                  __attribute__((always_inline)) {
+                  __attribute__((always_inline)) -> bool {
     if (kv0 >= w_key_end) {
       if constexpr (LATE_DMA) issue_next();
-      return;
+      return false;
     }
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
@@ -158,7 +190,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     const bool vec = Lk % 8 == 0 && whole;     // whole, aligned mask rows for the tile
     float t8[4][8];
     if constexpr (KIND != 0) {
-      if (PREF && vec) {
+      if (PREF_ADD && vec) {
+        // Terms loaded a tile ahead: read after the score products below.
+      } else if (PREF && vec) {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
@@ -179,6 +213,21 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
 #pragma unroll
       for (int t = 0; t < KS; ++t)
         s[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s[b]);
+    }
+    if constexpr (PREF_ADD) {
+      if (vec) {
+        // After the score products (fence), so that the wait for these loads
+        // comes as late as possible.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float4 x = am[2 * grp + (e >> 2)];
+            const float m = (e & 3) == 0 ? x.x : (e & 3) == 1 ? x.y : (e & 3) == 2 ? x.z : x.w;
+            t8[grp][e] = m * kLog2e;
+          }
+      }
     }
     // Register r of block b holds key kv0 + 32 b + 16 (r / 8) + 8 h + r % 8.
     unsigned keep[4] = {0xffu, 0xffu, 0xffu, 0xffu};
@@ -236,6 +285,13 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         pb[grp][e] = (short)round16<BF16>(!DROP || ((keep[grp] >> e) & 1u) ? p : 0.f);
       }
     }
+    bool loaded = false;
+    if constexpr (PREF_ADD) {
+      if (kv0 + BQ < w_key_end && am_vec(kv0 + BQ)) {
+        am_load(kv0 + BQ);
+        loaded = true;
+      }
+    }
     // The correction exp(d_old - d_new) is 1 unless a row's maximum moved
     // (or this is its first key): skip the multiplications when no row of
     // the wave needs them.
@@ -256,10 +312,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         oacc[db] = mfma32<BF16>(s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, pb[stp], oacc[db]);
       }
     }
+    return loaded;
   };
 
   uint2 rawA[4] = {}, rawB[4] = {};
   if constexpr (PREF) raw_load(0, rawA);
+  if constexpr (PREF_ADD) {
+    if (0 < w_key_end && am_vec(0)) am_load(0);
+  }
   land_all();
   if constexpr (PREF) raw_landed(rawA);
   __syncthreads();
@@ -271,8 +331,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
       if (j + 1 < nkt) issue(j + 1, smem + STAGE);
     };
     if constexpr (!LATE_DMA) next_a();
-    tile(smem, j * BQ, rawA, next_a);
-    land_all();
+    land(tile(smem, j * BQ, rawA, next_a));
     if constexpr (PREF) raw_landed(rawB);
     __syncthreads();
     if (j + 1 >= nkt) break;
@@ -283,8 +342,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
       if (j + 2 < nkt) issue(j + 2, smem);
     };
     if constexpr (!LATE_DMA) next_b();
-    tile(smem + STAGE, (j + 1) * BQ, rawB, next_b);
-    land_all();
+    land(tile(smem + STAGE, (j + 1) * BQ, rawB, next_b));
     if constexpr (PREF) raw_landed(rawA);
     __syncthreads();
   }
