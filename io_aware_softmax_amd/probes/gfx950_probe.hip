@@ -2,8 +2,9 @@
 // around on gfx950 (not part of the library): per-wave issue cost of the
 // softmax's VALU instructions and of one 32x32x16 bf16 MFMA, how much a
 // stream of MFMAs on one wave slows a VALU stream on the other wave of the
-// same SIMD, and per-wave LDS read throughput for the two read forms the
-// kernels use (ds_read_b128 and ds_read_b64_tr_b16).
+// same SIMD, per-wave LDS read throughput for the two read forms the
+// kernels use (ds_read_b128 and ds_read_b64_tr_b16), and the HBM read rate
+// of a plain stream of 16-byte loads, ordinary and nontemporal.
 //
 // Every workgroup reserves 96 KB of LDS, so at most one runs per compute
 // unit; the grid is 256 workgroups.  Each wave times its own loop with
@@ -162,6 +163,46 @@ __global__ __launch_bounds__(512) void probe(unsigned long long* out, float* sin
   if (keep == 1234.5f) sink[tid] = keep;  // never met for these inputs; keeps the work alive
 }
 
+// Reads n 16-byte vectors of `src` once (grid-stride), ordinary or
+// nontemporal loads, and folds them into one word per thread; the only
+// store sits behind a condition the data (all zero) never meets.
+template <bool NT>
+__global__ __launch_bounds__(256) void hbm_read(const u32x4* __restrict__ src, size_t n, unsigned* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  }
+  for (; i < n; i += stride) acc ^= NT ? __builtin_nontemporal_load(src + i) : src[i];
+  if ((acc.x | acc.y | acc.z | acc.w) == 0x5a5a5a5au) sink[threadIdx.x] = acc.x;
+}
+
+template <bool NT>
+double hbm_rate(const u32x4* buf, size_t n, unsigned* sink) {
+  const int grid = 256 * 16;  // 16 workgroups of 256 threads per compute unit
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) std::exit(1);
+  for (int r = 0; r < 3; ++r) hbm_read<NT><<<grid, 256>>>(buf, n, sink);  // warm-up
+  (void)hipEventRecord(e0, nullptr);
+  constexpr int kReps = 5;
+  for (int r = 0; r < kReps; ++r) hbm_read<NT><<<grid, 256>>>(buf, n, sink);
+  (void)hipEventRecord(e1, nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) {
+    std::fprintf(stderr, "hbm probe failed: %s\n", hipGetErrorString(hipGetLastError()));
+    std::exit(2);
+  }
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return double(n) * 16.0 * kReps / (ms * 1e-3) / 1e12;
+}
+
 const char* kNames[] = {"v_exp_f32", "v_fma_f32", "v_add_f32", "v_cvt_pk_bf16_f32", "v_max3_f32",
                         "v_mfma_f32_32x32x16_bf16", "softmax tile (112 VALU)", "ds_read_b128", "ds_read_b64_tr_b16"};
 // Instructions (or reads) per loop iteration of each stream.
@@ -271,5 +312,20 @@ int main() {
   alone<kLdsB128>(2);
   alone<kLdsTr>(1);
   alone<kLdsTr>(2);
+  {
+    const size_t bytes = size_t(8) << 30;
+    const size_t n = bytes / 16;
+    u32x4* buf = nullptr;
+    unsigned* sink = nullptr;
+    if (hipMalloc(&buf, bytes) != hipSuccess || hipMalloc(&sink, 256 * sizeof(unsigned)) != hipSuccess ||
+        hipMemset(buf, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      std::fprintf(stderr, "hbm buffer setup failed\n");
+      std::exit(1);
+    }
+    std::printf("HBM read of 8 GiB, 16-byte loads: ordinary %.2f TB/s, nontemporal %.2f TB/s\n",
+                hbm_rate<false>(buf, n, sink), hbm_rate<true>(buf, n, sink));
+    (void)hipFree(buf);
+    (void)hipFree(sink);
+  }
   return 0;
 }
