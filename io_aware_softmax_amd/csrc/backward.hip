@@ -501,10 +501,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
   // fetches the current tile again into the idle stage (never read).  Other
   // tiles (causal diagonal, Lq tail) issue the next tile's DMA first and go
   // block by block.
+  // FAST: the caller knows the tile takes the slot schedule.
   auto tile = [&](char* stage, int q0, char* nstage, int tn, const unsigned char (&mcur)[2][16],
-                  unsigned char (&mnext)[2][16]) __attribute__((always_inline)) {
+                  unsigned char (&mnext)[2][16], auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
     const bool has_next = tn < nqt;
-    if (!EX && q0 + BQ <= Lq && (!CAUSAL || q0 + off >= kw0 + 31)) {
+    if constexpr (FAST) {
       const int tf = has_next ? tn : tn - 1;
       const int rows_left = min(BQ, Lq - tf * BQ);
       unsigned cur[T::PER_WAVE];
@@ -550,18 +552,51 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
   land_all();
   if constexpr (PREF) mask_landed(mA);
   __syncthreads();
-  // Tiles alternate between the two stages; the loop body covers a pair so
-  // that every LDS address is a lane offset plus an immediate.
-  for (int t = t_begin; t < nqt; t += 2) {
-    tile(smem, t * BQ, smem + STAGE, t + 1, mA, mB);
+  // Tiles alternate between the two stages (tile t in stage (t - t_begin)
+  // mod 2); each loop body covers a pair so that every LDS address is a lane
+  // offset plus an immediate.  The tiles that take the slot schedule (whole,
+  // unmasked, at or past the wave's causal diagonal) form one contiguous
+  // range [t_lo, t_hi); the loops run the generic tiles before it, the
+  // range, and the generic tiles after it, so that each loop has one code
+  // path and the compiler one register assignment per loop (a branch
+  // between the two paths inside one loop made it shuffle the dK / dV
+  // accumulators between registers on every tile).  The slot loop starts at
+  // an even stage: a range starting at an odd one gives its first tile to
+  // the generic loop, and an odd tail goes to the last loop.  Every wave
+  // passes one barrier per tile whichever loop it is in.
+  const std::integral_constant<bool, true> fast{};
+  const std::integral_constant<bool, false> generic{};
+  int t_lo = nqt, t_hi = nqt;
+  if constexpr (!EX) {
+    const int first = CAUSAL ? max(t_begin, (max(0, kw0 + 31 - off) + BQ - 1) / BQ) : t_begin;
+    const int last = Lq / BQ;  // tiles before it are whole
+    if (first < last) {
+      t_lo = first + ((first - t_begin) & 1);
+      t_hi = t_lo + 2 * (max(0, last - t_lo) / 2);
+      if (t_lo >= t_hi) t_lo = t_hi = nqt;  // no pair left: every tile generic
+    }
+  }
+  t_lo = __builtin_amdgcn_readfirstlane(t_lo);
+  t_hi = __builtin_amdgcn_readfirstlane(t_hi);
+  auto pair = [&](int t, auto tag) __attribute__((always_inline)) -> bool {  // false: no tile after t
+    tile(smem, t * BQ, smem + STAGE, t + 1, mA, mB, tag);
     land_all();
     if constexpr (PREF) mask_landed(mB);
     __syncthreads();
-    if (t + 1 >= nqt) break;
-    tile(smem + STAGE, (t + 1) * BQ, smem, t + 2, mB, mA);
+    if (t + 1 >= nqt) return false;
+    tile(smem + STAGE, (t + 1) * BQ, smem, t + 2, mB, mA, tag);
     land_all();
     if constexpr (PREF) mask_landed(mA);
     __syncthreads();
+    return true;
+  };
+  int t = t_begin;
+  for (; t < t_lo; t += 2)  // (t_lo - t_begin) is even or t_lo == nqt
+    if (!pair(t, generic)) break;
+  if (t_lo < t_hi) {
+    for (t = t_lo; t < t_hi; t += 2) pair(t, fast);
+    for (; t < nqt; t += 2)
+      if (!pair(t, generic)) break;
   }
 
   // Register r of block db holds key kw0 + 8 (r / 4) + 4 h + r % 4,
