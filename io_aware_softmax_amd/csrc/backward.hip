@@ -714,8 +714,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
   const float c = a.c;
 
-  // One 32-key block b of the tile in `stage`.
-  auto block = [&](const char* stage, int kv0, int b) __attribute__((always_inline)) {
+  // One 32-key block b of the tile in `stage`.  MASKED: the tile may hold
+  // keys past Lk or (causal) past the diagonal of some query of the wave.
+  auto block = [&](const char* stage, int kv0, int b, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int kb0 = kv0 + 32 * b;
     if (kb0 >= w_key_end) return;
     const char* Ks = stage;
@@ -743,7 +745,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
       dp = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp);
     }
     // Register r holds key kb0 + 16 (r / 8) + 8 h + r % 8 of query qi.
-    const bool masked = kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off);
+    const bool masked = MASKED && (kb0 + 32 > Lk || (CAUSAL && kb0 + 31 > wq0 + off));
     s16x8 sa[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -772,19 +774,34 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
 
   land_all();
   __syncthreads();
-  for (int j = 0; j < nkt; j += 2) {
+  // Tiles alternate between the two stages; each loop body covers a pair so
+  // that every LDS address is a lane offset plus an immediate.  Tiles
+  // [0, j_plain) hold no key past Lk or past the diagonal of any query of
+  // the wave: they run without the masking code in a loop of their own (one
+  // code path per loop), an even number of them so that the second loop
+  // starts in the first stage.  Every wave passes one barrier per tile
+  // whichever loop it is in.
+  int j_plain = Lk / BQ;
+  if (CAUSAL) j_plain = min(j_plain, max(0, wq0 + off + 1) / BQ);
+  j_plain = __builtin_amdgcn_readfirstlane(min(j_plain, nkt) & ~1);
+  auto pair = [&](int j, auto tag) __attribute__((always_inline)) -> bool {  // false: no tile after j
     if (j + 1 < nkt) issue(j + 1, smem + STAGE);
-    block(smem, j * BQ, 0);
-    block(smem, j * BQ, 1);
+    block(smem, j * BQ, 0, tag);
+    block(smem, j * BQ, 1, tag);
     land_all();
     __syncthreads();
-    if (j + 1 >= nkt) break;
+    if (j + 1 >= nkt) return false;
     if (j + 2 < nkt) issue(j + 2, smem);
-    block(smem + STAGE, (j + 1) * BQ, 0);
-    block(smem + STAGE, (j + 1) * BQ, 1);
+    block(smem + STAGE, (j + 1) * BQ, 0, tag);
+    block(smem + STAGE, (j + 1) * BQ, 1, tag);
     land_all();
     __syncthreads();
-  }
+    return true;
+  };
+  int j = 0;
+  for (; j < j_plain; j += 2) pair(j, std::integral_constant<bool, false>{});
+  for (; j < nkt; j += 2)
+    if (!pair(j, std::integral_constant<bool, true>{})) break;
 
   // Register r of block db holds query wq0 + 8 (r / 4) + 4 h + r % 4,
   // column 32 db + n.
