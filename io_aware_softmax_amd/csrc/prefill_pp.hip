@@ -366,6 +366,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook);
     }
   };
+  // The last steps of an item (DMA issued in one go): a wave past its last
+  // tile (causal: the early rows of an item end a few tiles before its last)
+  // runs no products.
+  auto matrix_tail = [&](int j, auto issue_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(issue_tag)::value == 2) {
+      if (j + 2 < nkv) dma_k(kb(j + 2), (j + 2) * BN);
+      if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
+    }
+    if (j < w_nkv)
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook);
+  };
   auto matrix_first = [&]() __attribute__((always_inline)) {  // step -1: S_0 only
     matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook);
   };
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       if (j < j_spread) spread_step(j++);
       for (; j < nkv; ++j) {
         __builtin_amdgcn_s_setprio(1);
-        matrix(j, IssueUpfront{});
+        matrix_tail(j, IssueUpfront{});
         barrier_lds();
         __builtin_amdgcn_s_setprio(0);
         softmax_tile(j + 1);
@@ -549,12 +560,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         matrix(jj, NoIssue{});
         barrier_lds();
       };
+      // Full steps j < nkv - 1, two per iteration as for group 0; then the
+      // last step, which needs no scores.
       int j = 0;
-      for (; j + 1 < nkv; j += 2) {  // two steps per iteration, as for group 0
+      for (; j + 2 < nkv; j += 2) {
         step(j);
         step(j + 1);
       }
-      if (j < nkv) step(j);
+      if (j + 1 < nkv) step(j++);
+      if (j < nkv) {
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile(j);
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(1);
+        matrix_tail(j, NoIssue{});
+        barrier_lds();
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 
