@@ -772,6 +772,46 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     }
   };
 
+  // A whole tile without mask, dropout or masked keys (the plain
+  // backward's common case), software-pipelined over its two blocks: the
+  // S and dP products of block 1 are issued before the softmax work of
+  // block 0, so that the wave's MFMAs and VALU overlap even when the other
+  // wave of the SIMD is in the same phase.
+  auto tile_plain = [&](const char* stage) __attribute__((always_inline)) {
+    const char* Ks = stage;
+    const char* Vs = stage + T::BYTES;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x16{};
+      dp[b] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        s[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s[b]);
+        dp[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s16x8 sa[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -l2));
+        sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dp[b][r] - dd));
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int rowoff = (32 * b + 16 * s2) * T::PITCH;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const s16x4 lo = lds_read_tr(Ks + rowoff + ta[db][0]);
+          const s16x4 hi = lds_read_tr(Ks + rowoff + ta[db][1]);
+          dq[db] = mfma32<BF16>(sa[s2], s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, dq[db]);
+        }
+      }
+    }
+  };
+
   land_all();
   __syncthreads();
   // Tiles alternate between the two stages; each loop body covers a pair so
@@ -784,16 +824,22 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
   int j_plain = Lk / BQ;
   if (CAUSAL) j_plain = min(j_plain, max(0, wq0 + off + 1) / BQ);
   j_plain = __builtin_amdgcn_readfirstlane(min(j_plain, nkt) & ~1);
+  auto run_tile = [&](const char* stage, int kv0, auto tag) __attribute__((always_inline)) {
+    if constexpr (!EX && !decltype(tag)::value) {
+      tile_plain(stage);
+    } else {
+      block(stage, kv0, 0, tag);
+      block(stage, kv0, 1, tag);
+    }
+  };
   auto pair = [&](int j, auto tag) __attribute__((always_inline)) -> bool {  // false: no tile after j
     if (j + 1 < nkt) issue(j + 1, smem + STAGE);
-    block(smem, j * BQ, 0, tag);
-    block(smem, j * BQ, 1, tag);
+    run_tile(smem, j * BQ, tag);
     land_all();
     __syncthreads();
     if (j + 1 >= nkt) return false;
     if (j + 2 < nkt) issue(j + 2, smem);
-    block(smem + STAGE, (j + 1) * BQ, 0, tag);
-    block(smem + STAGE, (j + 1) * BQ, 1, tag);
+    run_tile(smem + STAGE, (j + 1) * BQ, tag);
     land_all();
     __syncthreads();
     return true;
