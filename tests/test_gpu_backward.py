@@ -90,6 +90,17 @@ def test_backward_rectangular(Lq, Lk, causal):
     _case(f"bwd_rect_{Lq}x{Lk}", 2, 2, Lq, Lk, 128, "bf16", causal, seed=Lq + 7 * Lk)
 
 
+@pytest.mark.parametrize("Lq,Lk,D,causal", [(768, 768, 128, True), (832, 832, 128, True), (640, 896, 128, True),
+                                            (832, 832, 128, False), (768, 832, 64, True)])
+def test_backward_tile_loops(Lq, Lk, D, causal):
+    """Whole query tiles only (Lq % 64 == 0), even and odd tile counts and
+    diagonal offsets: the dK/dV kernel splits its tiles into generic ones
+    before the slot-scheduled range, the range (which starts in the first
+    stage), and generic ones after it, per wave; the dQ kernel runs its
+    unmasked tiles in a loop of their own."""
+    _case(f"bwd_loops_{Lq}x{Lk}_D{D}_c{int(causal)}", 1, 2, Lq, Lk, D, "bf16", causal, seed=Lq + 3 * Lk + D)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_backward_sharp_weights(dtype):
     """Queries x8 on half the heads and scale 1: near one-hot weights."""

@@ -116,6 +116,18 @@ def test_additive_mask_aligned_no_dropout(D, dtype, causal):
           kind="add")
 
 
+@pytest.mark.parametrize("Lq,Lk,D,dtype", [(520, 520, 128, "bf16"), (200, 584, 128, "bf16"), (520, 520, 64, "f16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_additive_mask_aligned_ragged_tail(Lq, Lk, D, dtype, causal):
+    """Aligned rows (Lk % 8 == 0) whose last key tile is partial: the
+    whole tiles take the terms loaded a tile ahead, the last one its own
+    loads; with causal, waves stop at different tiles."""
+    B, H = 1, 2
+    mask = inputs.additive_mask(Lk + 3 * D, (1, H, Lq, Lk), neg_inf=0.15)
+    _case(f"add_tail_{Lq}x{Lk}_{dtype}_D{D}_c{int(causal)}", B, H, Lq, Lk, D, dtype, causal, seed=Lq + Lk + D,
+          mask=mask, kind="add")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_additive_mask_batch_broadcast(causal):
     B, H, Lq, Lk = 2, 3, 150, 260
