@@ -56,13 +56,27 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   const int Lq = a.Lq, Lk = a.Lk;
   const int off = Lk - Lq;
   const int nqb = (Lq + BW - 1) / BW;
-  // Consecutive query blocks of one head share an XCD (same K / V);
-  // causal: the last query blocks (the most keys) go first.
+  // Workgroups are dealt to the 8 XCDs round robin.  Each XCD takes the
+  // query blocks of a contiguous range of heads (same K / V in its L2);
+  // causal: the last query blocks (the most keys) go first.  Within the
+  // range, consecutive workgroups take consecutive query blocks of one head,
+  // except for a mask shared by the heads (mask_h == 1) with whole heads per
+  // XCD: then they take one query block of each head of the range in turn,
+  // so that the heads that run together read the same mask rows (one L2
+  // fill of those rows serves them all).
   const int total = a.BH * nqb;
   const int wg = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
-  const int bh = logical / nqb;
-  const int qblk = CAUSAL ? nqb - 1 - logical % nqb : logical % nqb;
+  int bh, qpos;
+  if (KIND != 0 && md.mask_h == 1 && a.BH % 8 == 0) {
+    const int hx = a.BH / 8, r = wg / 8;  // heads per XCD, position in the XCD's range
+    bh = (wg % 8) * hx + r % hx;
+    qpos = r / hx;
+  } else {
+    const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    bh = logical / nqb;
+    qpos = logical % nqb;
+  }
+  const int qblk = CAUSAL ? nqb - 1 - qpos : qpos;
   const int q0 = qblk * BW, wq0 = q0 + 32 * w;
   const int q_last = min(q0 + BW, Lq) - 1;
   const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
