@@ -232,10 +232,21 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
   // Workgroups are dealt to the 8 XCDs round robin: consecutive key blocks
   // of one head (which stream the same Q / dO) share an XCD and its L2.
   // Causal: the first key blocks see the most queries and go first.
+  // With a mask shared by the heads (mask_h == 1) and whole heads per XCD,
+  // an XCD's workgroups take one key block of each of its heads in turn, so
+  // that the heads running together read the same mask columns.
   const int total = a.BH * nkb;
   const int wg = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
-  const int bh = logical / nkb, kb = logical % nkb;
+  int bh, kb;
+  if (KIND != 0 && md.mask_h == 1 && a.BH % 8 == 0) {
+    const int hx = a.BH / 8, r = wg / 8;
+    bh = (wg % 8) * hx + r % hx;
+    kb = r / hx;
+  } else {
+    const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    bh = logical / nkb;
+    kb = logical % nkb;
+  }
   const int k0 = kb * BW, kw0 = k0 + 32 * w;
   const int t_begin = CAUSAL ? max(0, k0 - off) / BQ : 0;
 
@@ -639,11 +650,21 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
   const int nqt = (Lq + BQ - 1) / BQ;
   // Consecutive query blocks of one head share an XCD (same K / V);
   // causal: the last query blocks (the most keys) go first.
+  // A mask shared by the heads: query blocks of the XCD's heads in turn,
+  // as in the dK/dV kernel.
   const int total = a.BH * nqb;
   const int wg = blockIdx.x;
-  const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
-  const int bh = logical / nqb;
-  const int qblk = CAUSAL ? nqb - 1 - logical % nqb : logical % nqb;
+  int bh, qpos;
+  if (KIND != 0 && md.mask_h == 1 && a.BH % 8 == 0) {
+    const int hx = a.BH / 8, r = wg / 8;
+    bh = (wg % 8) * hx + r % hx;
+    qpos = r / hx;
+  } else {
+    const int logical = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
+    bh = logical / nqb;
+    qpos = logical % nqb;
+  }
+  const int qblk = CAUSAL ? nqb - 1 - qpos : qpos;
   const int q0 = qblk * BW, wq0 = q0 + 32 * w;
   const int q_last = min(q0 + BW, Lq) - 1;
   const int kv_end = CAUSAL ? min(Lk, q_last + off + 1) : Lk;
