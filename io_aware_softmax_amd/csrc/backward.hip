@@ -50,7 +50,7 @@ using namespace st;
 
 constexpr int NT = 256;   // threads per workgroup (4 waves)
 constexpr int BW = 128;   // rows owned by a workgroup (4 waves x 32)
-constexpr int kStatFloats = 2 * BQ;  // per stats tile: lse2[64], then Dv[64]
+constexpr int kStatFloats = 2 * BQ;  // per stats tile: lse2[64], then -Dv[64]
 
 // One stats tile (512 B) into LDS; lanes 32-63 fetch the same bytes again
 // into the following 512 B (a whole instruction, never read).
@@ -70,7 +70,9 @@ __device__ __forceinline__ float load16(const unsigned short* p) {
 
 
 // ---------------------------------------------------------------------------
-// stats: lse2 = lse * log2(e) and Dv = rowsum(dO o O), tile-blocked.
+// stats: lse2 = lse * log2(e) and -Dv = -rowsum(dO o O), tile-blocked.  Dv
+// is stored negated: the dP products of the kernels below start their
+// accumulation from it (dP - Dv without a subtraction per element).
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(NT) void bwd_stats_kernel(BwdArgs a) {
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(NT) void bwd_stats_kernel(BwdArgs a) {
   if (part == 0) {
     float* st = a.stats + (size_t)tile * kStatFloats;
     st[r] = qi < a.Lq ? a.lse[(size_t)bh * a.Lq + qi] * kLog2e : INFINITY;
-    st[BQ + r] = qi < a.Lq ? acc : 0.f;
+    st[BQ + r] = qi < a.Lq ? -acc : 0.f;
   }
 }
 
@@ -149,7 +151,20 @@ __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, 
   using S = BwdSlots<D>;
   s16x8 fr[S::N];
   f32x16 sc[2], dp[2];
-  float2 l2[2][8], dd[2][8];  // stats of element pair k, read PFS slots ahead
+  float2 l2[2][8];  // lse2 of element pair k, read PFS slots ahead
+  // -Dv of the block's 16 queries in accumulator order: the dP products
+  // start from it, so they end at dP - Dv.
+  f32x16 nd[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float* src = st + BQ + 32 * b + 16 * half + 8 * h;
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      nd[b][8 * half + 0] = x0.x; nd[b][8 * half + 1] = x0.y; nd[b][8 * half + 2] = x0.z; nd[b][8 * half + 3] = x0.w;
+      nd[b][8 * half + 4] = x1.x; nd[b][8 * half + 5] = x1.y; nd[b][8 * half + 6] = x1.z; nd[b][8 * half + 7] = x1.w;
+    }
   s16x8 pa[2][2], sa[2][2];
   auto read = [&](int i) __attribute__((always_inline)) {
     if (i < 2 * S::NS) {
@@ -169,17 +184,15 @@ __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, 
   auto stats = [&](int b, int k) __attribute__((always_inline)) {
     const int q = 32 * b + 16 * (k >> 2) + 8 * h + 2 * (k & 3);
     l2[b][k] = *reinterpret_cast<const float2*>(st + q);
-    dd[b][k] = *reinterpret_cast<const float2*>(st + BQ + q);
   };
   auto pair = [&](int b, int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = 2 * k + u;
       const float lse2 = u ? l2[b][k].y : l2[b][k].x;
-      const float dv_i = u ? dd[b][k].y : dd[b][k].x;
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][e], c, -lse2));
       pa[b][e >> 3][e & 7] = (short)round16<BF16>(p);
-      sa[b][e >> 3][e & 7] = (short)round16<BF16>(p * (dp[b][e] - dv_i));
+      sa[b][e >> 3][e & 7] = (short)round16<BF16>(p * dp[b][e]);  // dp holds dP - Dv
     }
   };
   static_for<S::PF>([&](auto I) __attribute__((always_inline)) { read(I); });
@@ -192,7 +205,7 @@ __device__ __forceinline__ void dkdv_tile_fast(const char* Qs, const char* dOs, 
     if (i < 2 * S::NS) {
       const int b = i / S::NS, j = i % S::NS, t = j >> 1;
       if (j & 1)
-        dp[b] = mfma32<BF16>(fr[i], vreg[t], t == 0 ? f32x16{} : dp[b]);
+        dp[b] = mfma32<BF16>(fr[i], vreg[t], t == 0 ? nd[b] : dp[b]);
       else
         sc[b] = mfma32<BF16>(fr[i], kreg[t], t == 0 ? f32x16{} : sc[b]);
     } else {
@@ -443,7 +456,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
       });
     }
     // Register r holds query qb + 16 (r / 8) + 8 h + r % 8 of key kw0 + n.
-    float l2[16], dd[16];
+    float l2[16], dd[16];  // lse2 and -Dv of the block's queries
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int base = 32 * b + 16 * hh + 8 * h;
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BwdArgs a, MaskDropout 
         pv = p * z;
         dpk = dpk * z;
       }
-      const float ds = p * (dpk - dd[r]);
+      const float ds = p * (dpk + dd[r]);  // dd holds -Dv
       pa[r >> 3][r & 7] = (short)round16<BF16>(pv);
       sa[r >> 3][r & 7] = (short)round16<BF16>(ds);
     }
@@ -698,7 +711,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     qreg[t] = __builtin_bit_cast(s16x8, xq);
     oreg[t] = __builtin_bit_cast(s16x8, xo);
   }
-  float l2 = INFINITY, dd = 0.f;
+  float l2 = INFINITY, dd = 0.f;  // lse2 and -Dv of the lane's query
   if (qi < Lq) {
     const float* st = a.stats + ((size_t)bh * nqt + qi / BQ) * kStatFloats;
     l2 = st[qi % BQ];
@@ -778,7 +791,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
       }
       float dpk = dp[r];
       if constexpr (DROP) dpk = ((keep[r >> 3] >> (r & 7)) & 1u) ? dpk * md.rp : 0.f;
-      sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dpk - dd));
+      sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dpk + dd));  // dd holds -Dv
     }
     // dQ += dS K over the block's 32 keys (2 k-steps).
 #pragma unroll
@@ -793,6 +806,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     }
   };
 
+  // -Dv of the lane's query in every register of an accumulator block: the
+  // plain tiles' dP products start from it.
+  f32x16 neg_dd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_dd[r] = dd;  // dd holds -Dv
   // A whole tile without mask, dropout or masked keys (the plain
   // backward's common case), software-pipelined over its two blocks: the
   // S and dP products of block 1 are issued before the softmax work of
@@ -805,7 +823,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       s[b] = f32x16{};
-      dp[b] = f32x16{};
+      dp[b] = neg_dd;  // the products accumulate onto -Dv: dP - Dv in one go
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         s[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Ks + 32 * b * T::PITCH + ra[t]), qreg[t], s[b]);
@@ -818,7 +836,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -l2));
-        sa[r >> 3][r & 7] = (short)round16<BF16>(p * (dp[b][r] - dd));
+        sa[r >> 3][r & 7] = (short)round16<BF16>(p * dp[b][r]);
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
