@@ -16,8 +16,10 @@ duration) is reported under ``decode``; the backward of the prefill
 workload (dQ, dK, dV through ``attn_bwd``, timed on its own) under
 ``backward``.  ``cpu_baseline`` times the float64
 CPU oracle on a bounded sample of the prefill workload (test infrastructure,
-never part of the timed path); ``parity`` compares the timed prefill's
-output on those heads with the oracle's.
+never part of the timed path), and the oracle's time per row on the
+long-context workload's sampled rows with a labelled extrapolation;
+``parity`` compares the timed prefill's output on those heads with the
+oracle's.
 """
 
 from __future__ import annotations
@@ -134,6 +136,24 @@ def _cpu_baseline(wl, heads: int, out=None, lse=None):
             "cpu": _cpu_model(),
             "sample": f"heads 0-{heads - 1} of {wl.H} (all {wl.Lq} rows) of the causal bf16 prefill, "
                       f"float64 NumPy, {dt:.1f} s for {flops:.3e} algorithmic flops"}
+    # The long-context workload (B1 H8 L65536 causal) on its 256 sampled rows
+    # per head: the oracle's time per row and a labelled extrapolation to
+    # every row (the sampled rows are uniform over the sequence, so their
+    # mean cost stands for the mean row).
+    wl5 = inputs.WORKLOADS["long_causal_bf16_64k"]
+    t5 = 0.0
+    n5 = 0
+    for h in range(wl5.H):
+        rows = inputs.sample_rows(wl5, h, 256)
+        qkv = {t: inputs.slab_values(wl5, t, 0, h)[None, None] for t in "qkv"}
+        t1 = time.perf_counter()
+        oracle.attention(qkv["q"], qkv["k"], qkv["v"], wl5.scale, wl5.causal, rows=rows)
+        t5 += time.perf_counter() - t1
+        n5 += len(rows)
+    base["long_context_sampled_rows"] = {
+        "workload": "causal bf16 B1 H8 L65536 D128", "rows": n5, "s": t5, "ms_per_row": 1e3 * t5 / n5,
+        "extrapolated_full_s": t5 / n5 * wl5.B * wl5.H * wl5.Lq,
+        "note": "oracle time on the 256 sampled rows per head; full-workload time extrapolated, not measured"}
     parity = None
     if out is not None:
         eo = er = el = 0.0
