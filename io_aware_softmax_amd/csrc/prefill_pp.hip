@@ -227,15 +227,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       w_nkv = __builtin_amdgcn_readfirstlane(max(0, min(w_nkv - jl, nkv)));
       j_mask = __builtin_amdgcn_readfirstlane(max(0, min(j_mask - jl, nkv)));
     }
-    // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].
     qi = wq0 + n;
-    const unsigned short* Qh = Q + (size_t)bh * Lq * D;
+  };
+  // Q^T fragment (B operand): lane (n, h) holds Q[qi][16t + 8h .. +8].  The
+  // loads are left in flight: nothing reads qreg before the item's first
+  // barrier (sign_q below, or the first product).  A row past Lq loads row
+  // Lq - 1 instead (finite scores; such rows are never stored).
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const unsigned short* Qr = Q + ((size_t)bh * Lq + min(qi, Lq - 1)) * D + 8 * h;
 #pragma unroll
-    for (int t = 0; t < T::KSTEPS; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi < Lq) x = *reinterpret_cast<const u32x4*>(Qh + (size_t)qi * D + 16 * t + 8 * h);
-      x ^= qsign;
-      qreg[t] = __builtin_bit_cast(s16x8, x);
+    for (int t = 0; t < T::KSTEPS; ++t)
+      qreg[t] = __builtin_bit_cast(s16x8, *reinterpret_cast<const u32x4*>(Qr + 16 * t));
+  };
+  // A negative scale runs as scale |c| on -Q (flipped sign bits), so that
+  // masked scores (-inf) keep weight 0.
+  auto sign_q = [&]() __attribute__((always_inline)) {
+    if (qsign != 0u) {
+#pragma unroll
+      for (int t = 0; t < T::KSTEPS; ++t)
+        qreg[t] = __builtin_bit_cast(s16x8, __builtin_bit_cast(u32x4, qreg[t]) ^ qsign);
     }
   };
 
@@ -419,19 +429,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       return;
     }
     if (__builtin_expect(t >= j_mask, 0)) {
-      // Per-lane key offset and query made opaque here, so the per-element
-      // bounds are not hoisted out of the tile loop (registers).
-      int hk = 8 * h, q = qi;
-      asm volatile("" : "+v"(hk), "+v"(q));
+      // Score r of block blk is key kv0 + 8h + (32 blk + 16 (r/8) + r%8);
+      // the lane's last allowed key (Lk - 1, or its query's diagonal) as an
+      // offset `lim` on that constant: one compare per score.
       const int kv0 = (SPLIT ? t + jl_s : t) * BN;
+      int lim = (CAUSAL ? min(Lk - 1, qi + off) : Lk - 1) - kv0 - 8 * h;
+      asm volatile("" : "+v"(lim));  // per tile: keeps the compares in the loop
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * blk + 16 * (r >> 3) + hk + (r & 7);
-          const bool ok = key < Lk && (!CAUSAL || key <= q + off);
-          if (!ok) sc[blk][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * blk + 16 * (r >> 3) + (r & 7) > lim) sc[blk][r] = -INFINITY;
     }
     // This lane's largest score of the tile (keys excluded above are -inf).
     auto lane_max = [&]() __attribute__((always_inline)) -> float {
@@ -494,10 +502,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   int logical = item_at(0);
   if (logical < 0) return;  // the whole workgroup: no barrier pending
   setup(logical);
-  if (grp == 0) {
-    first_tiles();
-    land(vb(0), 0);
-  }
+  if (grp == 0) first_tiles();
+  load_q();
+  if (grp == 0) land(vb(0), 0);
   for (;;) {
 #pragma unroll
     for (int i = 0; i < T::DBLK; ++i) oacc[i] = f32x16{};
@@ -505,6 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     l_run = 0.f;
     e_run = 0.f;
     barrier_lds();  // the item's first tiles have landed
+    sign_q();
 
     // ---- the two groups' schedules, as separate loops (each wave executes
     //      the same sequence of barriers) ----
@@ -600,10 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       logical = item_at(++round);
       if (logical < 0) break;
       setup(logical);
-      if (grp == 0) {
-        first_tiles();
-        land(vb(0), 0);
-      }
+      if (grp == 0) first_tiles();
+      load_q();
+      if (grp == 0) land(vb(0), 0);
       continue;
     }
     // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
@@ -627,18 +634,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
     unsigned short* Ow = O + ((size_t)bh * Lq + wq0) * D;  // this wave's rows
     const int rows_left = Lq - wq0;
+    // The next item's first tiles go first (their latency is the longest),
+    // then its Q loads, left in flight; then this item's rows are stored.
     logical = item_at(++round);
     if (logical >= 0) {
       setup(logical);
       if (grp == 0) first_tiles();
+      load_q();
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staged rows
     constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+    u32x4 orow[32 / ROWS];
 #pragma unroll
     for (int i = 0; i < 32 / ROWS; ++i) {
       const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
-      if (row < rows_left) *reinterpret_cast<u32x4*>(Ow + (size_t)row * D + chunk * 8) = v;
+      orow[i] = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+      if (row < rows_left) *reinterpret_cast<u32x4*>(Ow + (size_t)row * D + chunk * 8) = orow[i];
     }
     if (logical < 0) break;
     if (grp == 0) land(vb(0), 0);
