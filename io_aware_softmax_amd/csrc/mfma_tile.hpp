@@ -102,6 +102,9 @@ constexpr unsigned kDmaBias = 4096u;
 template <int G>
 __device__ __forceinline__ void dma_run(const char* gbase, const unsigned* voff, unsigned m0) {
   static_assert(G >= 1 && G <= 4, "one M0 run holds 1 to 4 instructions");
+  // Wave-uniform by contract; readfirstlane keeps it in an SGPR even where
+  // the compiler computed it in a VGPR (free when it already is an SGPR).
+  m0 = __builtin_amdgcn_readfirstlane(m0);
   if constexpr (G == 1)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %0\n"
                  :

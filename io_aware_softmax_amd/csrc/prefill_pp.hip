@@ -86,19 +86,30 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+#ifndef PP_DEFER
+#define PP_DEFER 2
+#endif
+// Value products a matrix phase leaves for after the barrier that ends it.
+// Their operands are already in registers, so they keep the MFMA pipe busy
+// while the other wave of the SIMD, now in its matrix phase, waits for its
+// first LDS operands.
+constexpr int kDefer = PP_DEFER;
+
 // Matrix phase of one wave: S = K_{j+1} Q^T (DO_S) and O~ += V_j^T P_j^T
 // (DO_PV), one MFMA per slot, each operand read PF slots ahead.  hook(i)
 // runs at the start of slot i (the DMA issue of the next tiles rides here:
 // the wave waits for the MFMA pipe anyway, so a stalled DMA issue costs
-// little).
-template <bool BF16, int D, bool DO_S, bool DO_PV, class Hook>
+// little).  With DO_PV, mid() (the barrier that ends the phase) runs before
+// the last kDefer products.
+template <bool BF16, int D, bool DO_S, bool DO_PV, class Hook, class Mid>
 __device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbase, const s16x8 (&qreg)[D / 16],
                                              f32x16 (&s)[2], const s16x8 (&pb)[4], f32x16 (&oacc)[D / 32],
-                                             Hook&& hook) {
+                                             Hook&& hook, Mid&& mid) {
   using T = Tile<D>;
   constexpr int NS = DO_S ? 2 * T::KSTEPS : 0;
   constexpr int NP = DO_PV ? 4 * T::DBLK : 0;
   constexpr int N = NS + NP;
+  static_assert(!DO_PV || kDefer < NP, "deferred products are value products");
   constexpr int PF = 6;
   s16x8 fr[N];
   auto read = [&](int r) __attribute__((always_inline)) {
@@ -117,6 +128,10 @@ __device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbas
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    if (DO_PV && i == N - kDefer) {
+      mid();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     hook(i);
     if (i + PF < N) read(i + PF);
     if (i < NS) {
@@ -353,6 +368,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     };
   };
   auto no_hook = [](int) __attribute__((always_inline)) {};
+  auto no_mid = []() __attribute__((always_inline)) {};
+  // The barrier that ends a matrix phase; the deferred products after it
+  // run at the softmax phase's issue priority.
+  auto end_phase = [&]() __attribute__((always_inline)) {
+    barrier_lds();
+    __builtin_amdgcn_s_setprio(0);
+  };
 
   // Matrix phase of step j: S_{j+1} and O~ += V_j P_j.  Every wave runs
   // both products on every step so that the loop has one code path: a wave
@@ -361,19 +383,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // Group 0 (issue = true) also issues the DMA of the tiles of step j+1.
   // issue_tag: 0 none (group 1), 1 spread over the slots (K_{j+2} and
   // V_{j+1} whole), 2 in one go before the phase (ragged or absent tiles).
+  // mid: the barrier that ends the phase (run before its last kDefer
+  // products; the caller runs none after the call).
   auto matrix = [&](int j, auto issue_tag) __attribute__((always_inline)) {
     constexpr int ISSUE = decltype(issue_tag)::value;
     if constexpr (ISSUE == 1) {
       const int jg = SPLIT ? j + jl_s : j;  // tile index in the head
       matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc,
                                         dma_hook(biased(Kb + (size_t)(jg + 2) * BN * (D * 2)), kb(j + 2),
-                                                 biased(Vb + (size_t)(jg + 1) * BN * (D * 2)), vb(j + 1)));
+                                                 biased(Vb + (size_t)(jg + 1) * BN * (D * 2)), vb(j + 1)),
+                                        end_phase);
     } else {
       if constexpr (ISSUE == 2) {
         if (j + 2 < nkv) dma_k(kb(j + 2), (j + 2) * BN);
         if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
       }
-      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook);
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook,
+                                        end_phase);
     }
   };
   // The last steps of an item (DMA issued in one go): a wave past its last
@@ -385,10 +411,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
     }
     if (j < w_nkv)
-      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook);
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook,
+                                        end_phase);
+    else
+      end_phase();
   };
   auto matrix_first = [&]() __attribute__((always_inline)) {  // step -1: S_0 only
-    matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook);
+    matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook, no_mid);
   };
   using NoIssue = std::integral_constant<int, 0>;
   using IssueSpread = std::integral_constant<int, 1>;
@@ -533,8 +562,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       auto spread_step = [&](int jj) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         matrix(jj, IssueSpread{});
-        barrier_lds();
-        __builtin_amdgcn_s_setprio(0);
         softmax_tile(jj + 1);
         land(vb(jj + 1), (jj + 1) * BN);
         barrier_lds();
@@ -549,8 +576,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       for (; j < nkv; ++j) {
         __builtin_amdgcn_s_setprio(1);
         matrix_tail(j, IssueUpfront{});
-        barrier_lds();
-        __builtin_amdgcn_s_setprio(0);
         softmax_tile(j + 1);
         if (j + 1 < nkv) land(vb(j + 1), (j + 1) * BN);
         barrier_lds();
@@ -566,7 +591,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
         matrix(jj, NoIssue{});
-        barrier_lds();
       };
       // Full steps j < nkv - 1, two per iteration as for group 0; then the
       // last step, which needs no scores.
@@ -582,7 +606,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
         matrix_tail(j, NoIssue{});
-        barrier_lds();
       }
     }
     __builtin_amdgcn_s_setprio(0);
