@@ -416,6 +416,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     else
       end_phase();
   };
+  // The item's last step (j = nkv - 1) needs no scores: value products only
+  // (none for a wave past its last tile); mid as for matrix_phase.
+  auto matrix_last = [&](int j, auto&& mid) __attribute__((always_inline)) {
+    if (j < w_nkv)
+      matrix_phase<BF16, D, false, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook, mid);
+    else
+      mid();
+  };
+  auto prio_low = []() __attribute__((always_inline)) { __builtin_amdgcn_s_setprio(0); };
   auto matrix_first = [&]() __attribute__((always_inline)) {  // step -1: S_0 only
     matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook, no_mid);
   };
@@ -527,8 +536,68 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     if (1 < nkv) dma_k(kb(1), BN);
   };
 
+  // ---- next item started during the current item's last step (unsplit
+  //      kernel): that step reads no K tile and no Q, so the next item's
+  //      Q, K_0, K_1 (and V_0 when the last V tile sits in the other
+  //      buffer) load while the last value products run, instead of all
+  //      waves sending their epilogue traffic through the memory pipe at
+  //      once.  The current item's output rows are saved first. ----
+  unsigned short* o_rows = nullptr;  // O row wq0 of the finishing item
+  float* l_rows = nullptr;           // its LSE row wq0
+  int rows_cur = 0;                  // its rows from wq0 on
+  bool v0_issued = false;            // V_0 of the next item already issued
   int round = 0;
   int logical = item_at(0);
+  auto begin_next = [&](bool issue_dma) __attribute__((always_inline)) {
+    o_rows = O + ((size_t)bh * Lq + wq0) * D;
+    l_rows = LSE + (size_t)bh * Lq + wq0;
+    rows_cur = Lq - wq0;
+    const int nkv_cur = nkv;
+    logical = item_at(++round);
+    if (logical >= 0) {
+      setup(logical);
+      if (issue_dma) {
+        dma_k(kb(0), 0);
+        if (1 < nkv) dma_k(kb(1), BN);
+        v0_issued = (nkv_cur & 1) == 0;  // the last V tile is in buffer 1
+        if (v0_issued) dma_v(vb(0), 0);
+      }
+      load_q();
+    }
+  };
+  // O = O~ / s and lse = ln 2 (d + log2 s) of the finishing item.  Each wave
+  // stages its 32 rows of O in LDS so that the global stores are whole
+  // 16-byte chunks of consecutive rows.
+  auto store_rows = [&]() __attribute__((always_inline)) {
+    char* ob = smem + LY::OST + w * 32 * LY::OPITCH;
+    const float l_tot = halves_sum(l_run);
+    const float inv = 1.f / (BF16 ? halves_sum(l_run - e_run) : l_tot);
+#pragma unroll
+    for (int db = 0; db < T::DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = 32 * db + 8 * jj + 4 * h;
+        const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
+        const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
+                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(ob + n * LY::OPITCH + d * 2) = make_uint2(lo, hi);
+      }
+    if (h == 0 && n < rows_cur) l_rows[n] = (m_ref + log2f(l_tot)) * kLn2;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staged rows
+    constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
+    u32x4 orow[32 / ROWS];
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+      orow[i] = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS; ++i) {
+      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
+      if (row < rows_cur) *reinterpret_cast<u32x4*>(o_rows + (size_t)row * D + chunk * 8) = orow[i];
+    }
+  };
   if (logical < 0) return;  // the whole workgroup: no barrier pending
   setup(logical);
   if (grp == 0) first_tiles();
@@ -573,12 +642,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         spread_step(j + 1);
       }
       if (j < j_spread) spread_step(j++);
-      for (; j < nkv; ++j) {
+      for (; j < (SPLIT ? nkv : nkv - 1); ++j) {
         __builtin_amdgcn_s_setprio(1);
         matrix_tail(j, IssueUpfront{});
         softmax_tile(j + 1);
         if (j + 1 < nkv) land(vb(j + 1), (j + 1) * BN);
         barrier_lds();
+      }
+      if constexpr (!SPLIT) {
+        // Last step: value products, then the next item's loads and this
+        // item's rows while group 1 finishes its value products.
+        __builtin_amdgcn_s_setprio(1);
+        matrix_last(j, end_phase);
+        begin_next(true);
+        store_rows();
+        barrier_lds();
+        if (logical >= 0 && !v0_issued) dma_v(vb(0), 0);  // buffer 0 read until now
       }
     } else {
       barrier_lds();
@@ -605,7 +684,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         softmax_tile(j);
         barrier_lds();
         __builtin_amdgcn_s_setprio(1);
-        matrix_tail(j, NoIssue{});
+        if constexpr (SPLIT) {
+          matrix_tail(j, NoIssue{});
+        } else {
+          matrix_last(j, prio_low);
+          begin_next(false);
+          store_rows();
+          barrier_lds();
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -636,48 +722,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       if (grp == 0) land(vb(0), 0);
       continue;
     }
-    // ---- epilogue: O = O~ / s, lse = ln 2 (d + log2 s) ----
-    // Each wave stages its 32 rows of O in LDS so that the global stores are
-    // whole 16-byte chunks of consecutive rows; the next item's first tiles
-    // and Q are loaded meanwhile (all tile reads of this item are done).
-    char* ob = smem + LY::OST + w * 32 * LY::OPITCH;
-    const float l_tot = halves_sum(l_run);
-    const float inv = 1.f / (BF16 ? halves_sum(l_run - e_run) : l_tot);
-#pragma unroll
-    for (int db = 0; db < T::DBLK; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = 32 * db + 8 * jj + 4 * h;
-        const unsigned lo = (unsigned)round16<BF16>(oacc[db][4 * jj + 0] * inv) |
-                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 1] * inv) << 16);
-        const unsigned hi = (unsigned)round16<BF16>(oacc[db][4 * jj + 2] * inv) |
-                            ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(ob + n * LY::OPITCH + d * 2) = make_uint2(lo, hi);
-      }
-    if (h == 0 && qi < Lq) LSE[(size_t)bh * Lq + qi] = (m_ref + log2f(l_tot)) * kLn2;
-    unsigned short* Ow = O + ((size_t)bh * Lq + wq0) * D;  // this wave's rows
-    const int rows_left = Lq - wq0;
-    // The next item's first tiles go first (their latency is the longest),
-    // then its Q loads, left in flight; then this item's rows are stored.
-    logical = item_at(++round);
-    if (logical >= 0) {
-      setup(logical);
-      if (grp == 0) first_tiles();
-      load_q();
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staged rows
-    constexpr int ROWS = 64 / T::CPR;  // rows per 64-lane store
-    u32x4 orow[32 / ROWS];
-#pragma unroll
-    for (int i = 0; i < 32 / ROWS; ++i) {
-      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
-      orow[i] = *reinterpret_cast<const u32x4*>(ob + row * LY::OPITCH + chunk * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 32 / ROWS; ++i) {
-      const int row = ROWS * i + lane / T::CPR, chunk = lane % T::CPR;
-      if (row < rows_left) *reinterpret_cast<u32x4*>(Ow + (size_t)row * D + chunk * 8) = orow[i];
-    }
+    // ---- unsplit: the rows were stored and the next item's loads issued
+    //      in the last step ----
     if (logical < 0) break;
     if (grp == 0) land(vb(0), 0);
   }
