@@ -626,7 +626,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       softmax_tile(0);
       barrier_lds();
       // Steps whose next tiles K_{j+2} and V_{j+1} are whole, then the rest.
-      const int j_spread = max(0, min(nkv - 2, Lk / BN - 2 - (SPLIT ? jl_s : 0)));
+      // Steps past the wave's last tile (j >= w_nkv, causal) run in the
+      // second loop, which leaves out their products.
+      const int j_spread = max(0, min(min(nkv - 2, w_nkv), Lk / BN - 2 - (SPLIT ? jl_s : 0)));
       int j = 0;
       auto spread_step = [&](int jj) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
@@ -671,14 +673,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         __builtin_amdgcn_s_setprio(1);
         matrix(jj, NoIssue{});
       };
-      // Full steps j < nkv - 1, two per iteration as for group 0; then the
-      // last step, which needs no scores.
+      // Full steps j < nkv - 1, two per iteration as for group 0, up to the
+      // wave's last tile; steps past it without products; then the last
+      // step, which needs no scores.
       int j = 0;
-      for (; j + 2 < nkv; j += 2) {
+      const int j_full = min(nkv - 1, w_nkv);
+      for (; j + 1 < j_full; j += 2) {
         step(j);
         step(j + 1);
       }
-      if (j + 1 < nkv) step(j++);
+      if (j < j_full) step(j++);
+      for (; j + 1 < nkv; ++j) {
+        __builtin_amdgcn_s_setprio(0);
+        softmax_tile(j);
+        barrier_lds();
+        __builtin_amdgcn_s_setprio(1);
+        matrix_tail(j, NoIssue{});
+      }
       if (j < nkv) {
         __builtin_amdgcn_s_setprio(0);
         softmax_tile(j);
