@@ -432,11 +432,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   using IssueSpread = std::integral_constant<int, 1>;
   using IssueUpfront = std::integral_constant<int, 2>;
 
-  // P = exp(a - d) for the 32 scores of this lane against the current
-  // reference, rounded to the MFMA type for the value product; returns the
-  // sum of the fp32 weights (the denominator sums those: exact LSE).
-  auto weights = [&]() __attribute__((always_inline)) -> float {
-    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+  // P = exp(a - d) for the 32 scores of this lane against the reference
+  // -neg_m, rounded to the MFMA type for the value product; returns the sum
+  // of the fp32 weights (the denominator sums those: exact LSE).
+  auto weights = [&](float neg_m) __attribute__((always_inline)) -> float {
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
@@ -493,19 +492,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     };
     // bf16: rounding error of the lane's largest weight, recomputed from its
     // largest score with the same arithmetic as weights() (bit-identical).
-    auto round_error = [&](float mx) __attribute__((always_inline)) -> float {
-      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+    auto round_error = [&](float mx, float neg_m) __attribute__((always_inline)) -> float {
       const float wmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, neg_m));
       return wmax - __builtin_bit_cast(float, (unsigned)round16<true>(wmax) << 16);
     };
+    // Common path: against the current reference.  A row without one
+    // (m_ref = -inf) gets weights +inf or NaN here, so its sum fails the
+    // check below and the weights are recomputed there.
     float mx_lane = BF16 ? lane_max() : 0.f;
-    float psum = weights();
-    float e_t = BF16 ? round_error(mx_lane) : 0.f;
+    float psum = weights(-m_ref);
+    float e_t = BF16 ? round_error(mx_lane, -m_ref) : 0.f;
     // The packed weights are complete before the check below, so the check
     // is the last thing of the phase on the common path.
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
-    if (__builtin_expect(__any(!(psum <= kTauWeight) || m_ref == -INFINITY), 0)) {
+    if (__builtin_expect(__any(!(psum <= kTauWeight)), 0)) {
       if constexpr (!BF16) mx_lane = lane_max();
       const float mx = halves_max(mx_lane);
       // The guide's running maximum d_k = max(d_{k-1}, max of chunk k)
@@ -522,8 +523,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       if constexpr (BF16) e_run *= alpha;
 #pragma unroll
       for (int i = 0; i < T::DBLK; ++i) oacc[i] *= alpha;
-      psum = weights();
-      if constexpr (BF16) e_t = round_error(mx_lane);
+      // A row still without a reference (every key so far masked, split
+      // key ranges only) keeps weight 0 for its masked scores.
+      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      psum = weights(neg_m);
+      if constexpr (BF16) e_t = round_error(mx_lane, neg_m);
     }
     l_run += psum;
     if constexpr (BF16) e_run += e_t;
