@@ -19,8 +19,8 @@
 // buffered, XOR-swizzled rows).  S^T = K Q^T puts 16 keys of the lane's
 // query in its registers, which are then directly the B operand (P^T) of
 // O^T += V^T P^T, V^T being read from LDS with ds_read_b64_tr_b16.  The mask
-// rows are read from device memory 8 keys at a time; the keep bits come from
-// two Philox4x32-10 blocks per 8 keys.
+// rows are read from device memory 8 keys at a time; the keep bits of 8 keys
+// come from one Philox4x32-10 block (a 16-bit half of a word per key).
 #include <hip/hip_runtime.h>
 #include <cmath>
 #include <cstdint>
