@@ -8,7 +8,10 @@ the cases below force that path on every few tiles (scores rising along the
 keys), never after the first tile (falling scores), and through an
 exponential that overflows to inf (scores of thousands).  The item schedule
 has three branches (one item per workgroup with and without per-XCD ranges,
-persistent workgroups over uneven ranges); each gets a case.  Bounds are the
+persistent workgroups over uneven ranges); each gets a case.  A persistent
+workgroup starts its next item inside the current item's last step; the
+transition cases reach its branches (V_0 of the next item issued early or
+after the step, one-tile items, rows past Lq, Lq < Lk).  Bounds are the
 documented ones: max |dO| 1e-2 (fp16), 2e-2 (bf16); LSE within
 1e-4 * max(1, |LSE_ref|).
 """
@@ -112,6 +115,27 @@ def test_item_schedules(H, L, causal):
     vals = {t: _normal((B, H, L, D), 800 + i + H) for i, t in enumerate("qkv")}
     say(f"case item schedule H{H} L{L} causal={causal}")
     _check(f"schedule H{H} L{L}", vals, "bf16", causal, 1.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("H,Lq,Lk,causal,dtype", [
+    (130, 320, 320, False, "bf16"),  # 5 key tiles: the last V tile in buffer 0, so V_0 of the next item waits
+    (130, 320, 320, True, "f16"),    # causal: items of 4 and 5 key tiles, a query tile with 64 live rows
+    (300, 48, 48, False, "bf16"),    # one key tile per item (the first step is also the last)
+    (300, 48, 48, True, "bf16"),
+    (300, 100, 200, True, "bf16"),   # Lq < Lk: bottom-right causal, ragged tiles, persistent
+])
+def test_item_transitions(H, Lq, Lk, causal, dtype):
+    """More items than resident workgroups, so each workgroup starts its next
+    item inside the last step of the current one: the next item's Q, K_0,
+    K_1 (and V_0 when the last V tile sits in the other buffer) load while
+    the last value products run.  The shapes reach an odd key-tile count
+    (V_0 issued after the last step), one-tile items, query tiles with rows
+    past Lq and a rectangular causal problem."""
+    B, D = 1, 128
+    vals = {"q": _normal((B, H, Lq, D), 950 + H), "k": _normal((B, H, Lk, D), 951 + H),
+            "v": _normal((B, H, Lk, D), 952 + H)}
+    say(f"case item transitions H{H} Lq{Lq} Lk{Lk} causal={causal} {dtype}")
+    _check(f"transitions H{H} {Lq}x{Lk} {dtype} c{int(causal)}", vals, dtype, causal, 1.0 / np.sqrt(D))
 
 
 @pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal", [
