@@ -17,17 +17,22 @@
 // 4-7 (group 1) run the same per-tile work half a step apart:
 //   matrix phase   S_{j+1} = K_{j+1} Q^T and O~ += V_j^T P_j^T (32 MFMAs at
 //                  D = 128, operands read from LDS a few MFMAs ahead);
-//   softmax phase  row maximum of S_{j+1}, lazy correction of O~ and s,
-//                  P_{j+1} = exp(a - d) rounded to the MFMA type, s += sum.
+//   softmax phase  P_{j+1} = exp(a - d) against the row's reference d,
+//                  rounded to the MFMA type, s += sum; the reference moves
+//                  (and O~, s are corrected) only when a weight sum says so.
 // While one wave of a SIMD is in its matrix phase the other is in its
 // softmax phase, so the MFMA pipe runs one wave's products while the vector
 // ALU runs the other wave's exponentials.  A workgroup barrier separates the
-// half steps; the matrix-phase wave runs at the higher issue priority.
-// Group 1 issues the K/V tile DMA (HBM -> LDS, no VGPR round trip) for the
-// next step during its softmax phase and waits for it at the end of the
-// following half step, so each DMA has a whole step to land.  K/V tiles are
+// half steps; the matrix-phase wave runs at the higher issue priority and
+// leaves its last two value products for after the barrier, where they
+// cover the other wave's wait for its first LDS operands.
+// Group 0 issues the K/V tile DMA (HBM -> LDS, no VGPR round trip) for the
+// next step during its matrix phase and waits for it at the end of its
+// softmax phase, so each DMA has most of a step to land.  K/V tiles are
 // double buffered: step j reads K_{j+1} and V_j while K_{j+2} and V_{j+1}
-// land.
+// land.  A persistent workgroup starts its next item inside the current
+// item's last step (which needs neither scores nor Q): the next Q, K_0,
+// K_1 and V_0 load while the last value products run.
 //
 // Register layout (per wave, as in the single-group kernel): Q^T is the B
 // operand of v_mfma_f32_32x32x16; K rows are read with bits 2 and 3 of the
