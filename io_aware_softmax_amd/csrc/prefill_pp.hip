@@ -439,16 +439,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
 
   // P = exp(a - d) for the 32 scores of this lane against the reference
   // -neg_m, rounded to the MFMA type for the value product; returns the sum
-  // of the fp32 weights (the denominator sums those: exact LSE).
-  auto weights = [&](float neg_m) __attribute__((always_inline)) -> float {
-    float psum = 0.f;
+  // of the fp32 weights (the denominator sums those: exact LSE) and, for
+  // bf16, the lane's largest weight in wmax.
+  auto weights = [&](float neg_m, float& wmax) __attribute__((always_inline)) -> float {
+    float psum = 0.f, mx = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int st = e >> 3, blk = st >> 1, r = 8 * (st & 1) + (e & 7);
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
       pb[st][e & 7] = (short)round16<BF16>(p);
       psum += p;
+      if constexpr (BF16) mx = fmaxf(mx, p);
     }
+    wmax = mx;
     return psum;
   };
 
@@ -495,25 +498,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         }
       return mx;
     };
-    // bf16: rounding error of the lane's largest weight, recomputed from its
-    // largest score with the same arithmetic as weights() (bit-identical).
-    auto round_error = [&](float mx, float neg_m) __attribute__((always_inline)) -> float {
-      const float wmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, neg_m));
+    // bf16: rounding error of the lane's largest weight (the weights are
+    // monotone in the scores, so this is the weight of its largest score).
+    auto round_error = [&](float wmax) __attribute__((always_inline)) -> float {
       return wmax - __builtin_bit_cast(float, (unsigned)round16<true>(wmax) << 16);
     };
     // Common path: against the current reference.  A row without one
     // (m_ref = -inf) gets weights +inf or NaN here, so its sum fails the
     // check below and the weights are recomputed there.
-    float mx_lane = BF16 ? lane_max() : 0.f;
-    float psum = weights(-m_ref);
-    float e_t = BF16 ? round_error(mx_lane, -m_ref) : 0.f;
+    float wmax;
+    float psum = weights(-m_ref, wmax);
+    float e_t = BF16 ? round_error(wmax) : 0.f;
     // The packed weights are complete before the check below, so the check
     // is the last thing of the phase on the common path.
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
     if (__builtin_expect(__any(!(psum <= kTauWeight)), 0)) {
-      if constexpr (!BF16) mx_lane = lane_max();
-      const float mx = halves_max(mx_lane);
+      const float mx = halves_max(lane_max());
       // The guide's running maximum d_k = max(d_{k-1}, max of chunk k)
       // with headroom: a row whose tile maximum passed its reference moves
       // the reference kHeadroom above that maximum and corrects O~ and s by
@@ -531,8 +532,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       // A row still without a reference (every key so far masked, split
       // key ranges only) keeps weight 0 for its masked scores.
       const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      psum = weights(neg_m);
-      if constexpr (BF16) e_t = round_error(mx_lane, neg_m);
+      psum = weights(neg_m, wmax);
+      if constexpr (BF16) e_t = round_error(wmax);
     }
     l_run += psum;
     if constexpr (BF16) e_run += e_t;
