@@ -68,14 +68,49 @@ constexpr float kTauWeight = 256.f;
 template <bool BF16>
 constexpr float kHeadroom = BF16 ? 24.f : 0.f;
 
+// V tile in LDS.  D = 128: unpadded rows of 256 B whose four 64-byte
+// granules are XOR-swizzled by the row's low two bits (granule g of row r at
+// g ^ (r mod 4)); the four rows x 64 B of one half-wave transposed read then
+// fall in four different granules, i.e. disjoint banks, and the tile is 16
+// whole DMA instructions.  D = 64 keeps the padded rows of Tile.
+template <int D>
+struct VTile {
+  static constexpr bool SWZ = D == 128;
+  static constexpr int SPR = SWZ ? D / 8 : Tile<D>::VSPR;  // 16-byte slots per row
+  static constexpr int PITCH = SPR * 16;
+  static constexpr int BYTES = BN * PITCH;
+  static constexpr int INST = BN * SPR / 64;
+  // Source offset, within the tile in device memory, of the 16 bytes that
+  // lane `lane` of DMA instruction `inst` writes to LDS slot 64 inst + lane.
+  __device__ static unsigned src_offset(int inst, int lane) {
+    if constexpr (SWZ) {
+      const int row = 4 * inst + (lane >> 4);  // 4 rows per instruction
+      const int pchunk = lane & 15;            // physical 16-byte chunk in the row
+      const int lchunk = 4 * ((pchunk >> 2) ^ (row & 3)) + (pchunk & 3);
+      return (unsigned)row * (D * 2) + (unsigned)lchunk * 16;
+    } else {
+      return dma_src_offset<D>(inst, lane, SPR);
+    }
+  }
+  // LDS byte offset (within a V tile) of this lane's transposed read of
+  // 32-column block db for key row `row` (row mod 4 = the lane's rows').
+  __device__ static int read_offset(int row, int db, int colbyte) {
+    if constexpr (SWZ)
+      return row * PITCH + ((db ^ (row & 3)) * 64) + colbyte;
+    else
+      return row * PITCH + 64 * db + colbyte;
+  }
+};
+
 template <int D>
 struct Layout {
   using T = Tile<D>;
+  using VT = VTile<D>;
   static constexpr int K0 = 0;
   static constexpr int K1 = T::KBYTES;
   static constexpr int V0 = 2 * T::KBYTES;
-  static constexpr int V1 = 2 * T::KBYTES + T::VBYTES;
-  static constexpr int KV = 2 * (T::KBYTES + T::VBYTES);
+  static constexpr int V1 = 2 * T::KBYTES + VT::BYTES;
+  static constexpr int KV = 2 * (T::KBYTES + VT::BYTES);
   static constexpr int OPITCH = D * 2 + 16;  // staging pitch of O rows
   static constexpr int OST = KV;             // O staging, apart from the tiles so that the
                                              // next item's tiles can land meanwhile
@@ -107,7 +142,8 @@ constexpr int kDefer = PP_DEFER;
 // little).  With DO_PV, mid() (the barrier that ends the phase) runs before
 // the last kDefer products.
 template <bool BF16, int D, bool DO_S, bool DO_PV, class Hook, class Mid>
-__device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbase, const s16x8 (&qreg)[D / 16],
+__device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbase, const int (&vl)[D / 32],
+                                             const s16x8 (&qreg)[D / 16],
                                              f32x16 (&s)[2], const s16x8 (&pb)[4], f32x16 (&oacc)[D / 32],
                                              Hook&& hook, Mid&& mid) {
   using T = Tile<D>;
@@ -122,9 +158,9 @@ __device__ __forceinline__ void matrix_phase(const char* kbase, const char* vbas
       fr[r] = *reinterpret_cast<const s16x8*>(kbase + 32 * (r & 1) * T::KPITCH + 32 * (r >> 1));
     } else {
       const int x = r - NS, st = x / T::DBLK, db = x % T::DBLK;
-      const char* p = vbase + 16 * st * T::VPITCH + 64 * db;
+      const char* p = vbase + vl[db] + 16 * st * VTile<D>::PITCH;
       const s16x4 lo = lds_read_tr(p);
-      const s16x4 hi = lds_read_tr(p + 4 * T::VPITCH);
+      const s16x4 hi = lds_read_tr(p + 4 * VTile<D>::PITCH);
       fr[r] = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
@@ -163,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   using T = Tile<D>;
   using LY = Layout<D>;
   using KP = DmaPlan<T::KINST, kRun, kDmaWaves>;
-  using VP = DmaPlan<T::VINST, kRun, kDmaWaves>;
+  using VP = DmaPlan<LY::VT::INST, kRun, kDmaWaves>;
   __shared__ __attribute__((aligned(16))) char smem[LY::TOTAL];
   auto kb = [&](int i) __attribute__((always_inline)) -> char* { return smem + ((i & 1) ? LY::K1 : LY::K0); };
   auto vb = [&](int i) __attribute__((always_inline)) -> char* { return smem + ((i & 1) ? LY::V1 : LY::V0); };
@@ -278,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     k_src[i] = dma_src_offset<D>(KP::inst(i, wd), lane, T::KSPR) + kDmaBias - KP::pos_in_run(i) * 1024u;
 #pragma unroll
   for (int i = 0; i < VP::N; ++i)
-    v_src[i] = dma_src_offset<D>(VP::inst(i, wd), lane, T::VSPR) + kDmaBias - VP::pos_in_run(i) * 1024u;
+    v_src[i] = LY::VT::src_offset(VP::inst(i, wd), lane) + kDmaBias - VP::pos_in_run(i) * 1024u;
   auto biased = [](const char* p) __attribute__((always_inline)) {
     return reinterpret_cast<const char*>(reinterpret_cast<uintptr_t>(p) - kDmaBias);
   };
@@ -308,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       for (int i = 0; i < VP::N; ++i) {
         if (i < VP::U || wd < VP::X) {
           const int slot = VP::inst(i, wd) * 64 + lane;
-          if (kv0 + slot / T::VSPR >= Lk) *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
+          if (kv0 + slot / LY::VT::SPR >= Lk) *reinterpret_cast<u32x4*>(vbuf + slot * 16) = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
@@ -339,7 +375,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   const int prow = (n & 0x13) | ((n & 4) << 1) | ((n & 8) >> 1);
   const int g = lane >> 4, li = lane & 15;
   const int k_lane = prow * T::KPITCH + 16 * h;
-  const int v_lane = (8 * h + (li >> 2)) * T::VPITCH + (16 * (g & 1) + 4 * (li & 3)) * 2;
+  // Transposed V reads: lane rows 8h + li/4 (+ 16 per k-step, + 4 for the
+  // upper half), bytes 32 (g & 1) + 8 (li & 3) of each 64-byte column block.
+  int v_lane[T::DBLK];
+#pragma unroll
+  for (int db = 0; db < T::DBLK; ++db)
+    v_lane[db] = LY::VT::read_offset(8 * h + (li >> 2), db, (16 * (g & 1) + 4 * (li & 3)) * 2);
 
   // DMA of K_{j+2} and V_{j+1} by a group-0 wave, spread over the slots
   // of its matrix phase (runs of kRun instructions; the extra instruction
@@ -394,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
     constexpr int ISSUE = decltype(issue_tag)::value;
     if constexpr (ISSUE == 1) {
       const int jg = SPLIT ? j + jl_s : j;  // tile index in the head
-      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc,
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j), v_lane, qreg, sc, pb, oacc,
                                         dma_hook(biased(Kb + (size_t)(jg + 2) * BN * (D * 2)), kb(j + 2),
                                                  biased(Vb + (size_t)(jg + 1) * BN * (D * 2)), vb(j + 1)),
                                         end_phase);
@@ -403,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
         if (j + 2 < nkv) dma_k(kb(j + 2), (j + 2) * BN);
         if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
       }
-      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook,
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j), v_lane, qreg, sc, pb, oacc, no_hook,
                                         end_phase);
     }
   };
@@ -416,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       if (j + 1 < nkv) dma_v(vb(j + 1), (j + 1) * BN);
     }
     if (j < w_nkv)
-      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook,
+      matrix_phase<BF16, D, true, true>(kb(j + 1) + k_lane, vb(j), v_lane, qreg, sc, pb, oacc, no_hook,
                                         end_phase);
     else
       end_phase();
@@ -425,13 +466,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
   // (none for a wave past its last tile); mid as for matrix_phase.
   auto matrix_last = [&](int j, auto&& mid) __attribute__((always_inline)) {
     if (j < w_nkv)
-      matrix_phase<BF16, D, false, true>(kb(j + 1) + k_lane, vb(j) + v_lane, qreg, sc, pb, oacc, no_hook, mid);
+      matrix_phase<BF16, D, false, true>(kb(j + 1) + k_lane, vb(j), v_lane, qreg, sc, pb, oacc, no_hook, mid);
     else
       mid();
   };
   auto prio_low = []() __attribute__((always_inline)) { __builtin_amdgcn_s_setprio(0); };
   auto matrix_first = [&]() __attribute__((always_inline)) {  // step -1: S_0 only
-    matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0) + v_lane, qreg, sc, pb, oacc, no_hook, no_mid);
+    matrix_phase<BF16, D, true, false>(kb(0) + k_lane, vb(0), v_lane, qreg, sc, pb, oacc, no_hook, no_mid);
   };
   using NoIssue = std::integral_constant<int, 0>;
   using IssueSpread = std::integral_constant<int, 1>;
