@@ -24,29 +24,32 @@ __device__ __forceinline__ size_t mask_slab(const MaskDropout& md, int bh, int L
 }
 
 // Terms of keys j0 .. j0 + 7 of one query row (idx = slab + i Lk + j0) for a
-// mask of kind KIND (0 none, 1 boolean, 2 additive); keys at or past Lk get
-// -inf.  `vec` (wave-uniform: Lk % 8 == 0 and all 8 keys before Lk) selects
+// mask of kind KIND (0 none, 1 boolean, 2 additive), in base-2 units and
+// shifted by `off` (a kept key gets off, an additive term off + log2(e) m);
+// keys at or past Lk get -inf.  `vec` (wave-uniform: Lk % 8 == 0 and all 8 keys before Lk) selects
 // one 8-byte (boolean) or two 16-byte (additive) loads; otherwise 8 element
 // loads, each from an index clamped into the row so that no load depends on
 // a lane condition.
 template <int KIND>
 __device__ __forceinline__ void mask_terms8_kind(const MaskDropout& md, size_t idx, int j0, int Lk, bool vec,
-                                                 float (&t)[8]) {
+                                                 float (&t)[8], float off = 0.f) {
   if constexpr (KIND == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? 0.f : -INFINITY;
+    for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? off : -INFINITY;
     return;
   } else {
     if (vec) {
       if constexpr (KIND == 1) {
         const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(md.mask) + idx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (((e < 4 ? u.x : u.y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
+        for (int e = 0; e < 8; ++e) t[e] = (((e < 4 ? u.x : u.y) >> (8 * (e & 3))) & 0xffu) ? off : -INFINITY;
       } else {
         const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx);
         const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(md.mask) + idx + 4);
-        t[0] = a.x * kLog2e; t[1] = a.y * kLog2e; t[2] = a.z * kLog2e; t[3] = a.w * kLog2e;
-        t[4] = b.x * kLog2e; t[5] = b.y * kLog2e; t[6] = b.z * kLog2e; t[7] = b.w * kLog2e;
+        t[0] = __builtin_fmaf(a.x, kLog2e, off); t[1] = __builtin_fmaf(a.y, kLog2e, off);
+        t[2] = __builtin_fmaf(a.z, kLog2e, off); t[3] = __builtin_fmaf(a.w, kLog2e, off);
+        t[4] = __builtin_fmaf(b.x, kLog2e, off); t[5] = __builtin_fmaf(b.y, kLog2e, off);
+        t[6] = __builtin_fmaf(b.z, kLog2e, off); t[7] = __builtin_fmaf(b.w, kLog2e, off);
       }
       return;
     }
@@ -59,14 +62,14 @@ __device__ __forceinline__ void mask_terms8_kind(const MaskDropout& md, size_t i
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = m8[ie[e]];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = (j0 + e < Lk && v[e] != 0) ? 0.f : -INFINITY;
+      for (int e = 0; e < 8; ++e) t[e] = (j0 + e < Lk && v[e] != 0) ? off : -INFINITY;
     } else {
       const float* m32 = static_cast<const float*>(md.mask);
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = m32[ie[e]];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? v[e] * kLog2e : -INFINITY;
+      for (int e = 0; e < 8; ++e) t[e] = j0 + e < Lk ? __builtin_fmaf(v[e], kLog2e, off) : -INFINITY;
     }
   }
 }

@@ -8,11 +8,14 @@
 // past Lk, or (causal) past the bottom-right diagonal; an additive mask is
 // added to the scaled scores.  The softmax statistics are the online ones of
 // the quidproquo.cc guide ("Mechanism: run with the wrong answer, then
-// correct it": running maximum d, denominator s, output corrected by
+// correct it": reference d, denominator s, output corrected by
 // exp(d_old - d_new)) over the un-dropped weights, so LSE does not depend on
 // dropout; the weights that enter the value product are the kept ones, and
-// O is scaled by 1 / (1 - p) at the end.  A row with no key left gets O = 0
-// and LSE = -inf.
+// O is scaled by 1 / (1 - p) at the end.  As in the plain prefill, d is a
+// lazy bound: it moves (above the tile maximum, by a headroom) only when a
+// weight sum of the wave passes 2^8, so the common tile computes no maximum
+// and folds -d into the mask term, one fma per score before the exp.  A row
+// with no key left gets O = 0 and LSE = -inf.
 //
 // Work decomposition: one workgroup = 4 waves x 32 queries; lane (n, h) of a
 // wave owns query n.  64-key tiles of K and V go HBM -> LDS by DMA (double
@@ -129,8 +132,17 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // running maximum (base-2 units), same in both halves
-  float l_run = 0.f;        // this half's share of the denominator
+  // Reference d of the row (base-2 units of the scaled, masked scores; the
+  // same in both halves) and this half's share of the denominator s,
+  // relative to d.  The reference moves only when a weight sum of the
+  // wave passes 2^8 (or a row has none yet), as in the plain kernel.
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  // bf16: sum of the rounding errors w - bf16(w) of each lane's largest kept
+  // weight per tile.  The value product takes the rounded weights and s the
+  // unrounded ones; with the reference above the maximum the largest weight
+  // is no longer exactly 1, so its rounding would reach O unmatched.
+  float e_run = 0.f;
 
   // Boolean masks: the raw bytes of a whole, aligned tile are loaded one
   // tile ahead, before that tile's K/V DMA is issued.  The compiler does not
@@ -202,6 +214,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
     // that the loads overlap them.
     const bool whole = kv0 + BQ <= Lk;        // no key of the tile at or past Lk
     const bool vec = Lk % 8 == 0 && whole;     // whole, aligned mask rows for the tile
+    // Every term carries -d, so one fma per score gives exp2's argument
+    // (no reference yet: 0, and the weights are recomputed below).
+    const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
     float t8[4][8];
     if constexpr (KIND != 0) {
       if (PREF_ADD && vec) {
@@ -211,12 +226,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            t8[grp][e] = (((e < 4 ? raw[grp].x : raw[grp].y) >> (8 * (e & 3))) & 0xffu) ? 0.f : -INFINITY;
+            t8[grp][e] = (((e < 4 ? raw[grp].x : raw[grp].y) >> (8 * (e & 3))) & 0xffu) ? nm : -INFINITY;
       } else {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           const int key0 = kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h;
-          mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, vec, t8[grp]);
+          mask_terms8_kind<KIND>(md, mrow + key0, key0, Lk, vec, t8[grp], nm);
         }
       }
     }
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
           for (int e = 0; e < 8; ++e) {
             const float4 x = am[2 * grp + (e >> 2)];
             const float m = (e & 3) == 0 ? x.x : (e & 3) == 1 ? x.y : (e & 3) == 2 ? x.z : x.w;
-            t8[grp][e] = m * kLog2e;
+            t8[grp][e] = __builtin_fmaf(m, kLog2e, nm);
           }
       }
     }
@@ -258,7 +273,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         if constexpr (KIND != 0)
           s[b][r] = __builtin_fmaf(s[b][r], c, t8[grp][e]);
         else
-          s[b][r] *= c;
+          s[b][r] = __builtin_fmaf(s[b][r], c, nm);
       }
     if constexpr (LATE_DMA) issue_next();
     // Keys past Lk (without a mask: only in the last tile) and, in tiles
@@ -277,28 +292,29 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         for (int e = 0; e < 8; ++e)
           if (kv0 + 32 * (grp >> 1) + 16 * (grp & 1) + 8 * h + e > qi + off) s[grp >> 1][8 * (grp & 1) + e] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
+    // Weights exp2(a - d) of the un-dropped scores (their sum is s), the
+    // kept ones rounded to the MFMA type for the value product, and (bf16)
+    // the rounding error of the lane's largest kept weight.
+    float psum = 0.f, e_t = 0.f;
     s16x8 pb[4];
+    auto weights = [&]() __attribute__((always_inline)) {
+      psum = 0.f;
+      float wmax = 0.f;
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int b = grp >> 1, half = grp & 1;
+      for (int grp = 0; grp < 4; ++grp) {
+        const int b = grp >> 1, half = grp & 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[b][8 * half + e] - m_use);
-        psum += p;
-        pb[grp][e] = (short)round16<BF16>(!DROP || ((keep[grp] >> e) & 1u) ? p : 0.f);
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[b][8 * half + e]);
+          psum += p;
+          const float w = !DROP || ((keep[grp] >> e) & 1u) ? p : 0.f;
+          if constexpr (BF16) wmax = fmaxf(wmax, w);
+          pb[grp][e] = (short)round16<BF16>(w);
+        }
       }
-    }
+      if constexpr (BF16) e_t = wmax - __builtin_bit_cast(float, (unsigned)round16<true>(wmax) << 16);
+    };
+    weights();
     bool loaded = false;
     if constexpr (PREF_ADD) {
       if (kv0 + BQ < w_key_end && am_vec(kv0 + BQ)) {
@@ -306,15 +322,38 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
         loaded = true;
       }
     }
-    // The correction exp(d_old - d_new) is 1 unless a row's maximum moved
-    // (or this is its first key): skip the multiplications when no row of
-    // the wave needs them.
-    if (__any(alpha != 1.f)) {
+    // Every weight of a lane is at most its sum: with no sum above 2^8 (and
+    // every row with a reference) the weights are bounded and d stays.
+    // Otherwise the guide's running maximum d_k = max(d_{k-1}, tile max),
+    // with headroom: a row whose tile maximum passed d moves d kHeadroom
+    // above it, O~ and s take the correction exp(d_old - d_new), and the
+    // weights are redone from the scores (still in s, shifted by -d).
+    if (__builtin_expect(__any(!(psum <= 256.f) || m_ref == -INFINITY), 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      mx = halves_max(mx == -INFINITY ? -INFINITY : mx - nm);
+      const bool grow = mx > m_ref;
+      const float m_new = grow ? mx + (BF16 ? 24.f : 0.f) : m_ref;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+      m_ref = m_new;
       l_run *= alpha;
+      if constexpr (BF16) e_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      // Shift the scores from -d_old to -d_new (a row without a reference
+      // yet keeps 0); rows that did not move add exactly 0.
+      const float delta = (m_ref == -INFINITY ? 0.f : -m_ref) - nm;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b][r] += delta;
+      weights();
     }
     l_run += psum;
+    if constexpr (BF16) e_run += e_t;
     // O^T += V^T P^T over the tile's four 16-key k-steps.
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
@@ -363,8 +402,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
 
   // Register r of block db holds column 32 db + 8 (r / 4) + 4 h + r % 4 of
   // the lane's query.
+  // O divides by s less the rounding errors of the largest weights (bf16);
+  // LSE takes s itself.
   const float l_tot = halves_sum(l_run);
-  const float inv = l_tot > 0.f ? (DROP ? md.rp : 1.f) / l_tot : 0.f;
+  const float l_o = BF16 ? l_tot - halves_sum(e_run) : l_tot;
+  const float inv = l_tot > 0.f ? (DROP ? md.rp : 1.f) / l_o : 0.f;
   if (qi < Lq) {
     unsigned short* Og = static_cast<unsigned short*>(a.o) + ((size_t)bh * Lq + qi) * D;
 #pragma unroll
@@ -377,7 +419,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
                             ((unsigned)round16<BF16>(oacc[db][4 * jj + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(Og + 32 * db + 8 * jj + 4 * h) = make_uint2(lo, hi);
       }
-    if (h == 0) a.lse[(size_t)bh * Lq + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (h == 0) a.lse[(size_t)bh * Lq + qi] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
