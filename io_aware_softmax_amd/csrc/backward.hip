@@ -820,6 +820,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
     const char* Ks = stage;
     const char* Vs = stage + T::BYTES;
     f32x16 s[2], dp[2];
+    // The S and dP products at raised priority: the SIMD's other wave
+    // (another workgroup) issues its VALU work in their shadow instead of
+    // contending for the matrix unit (+0.5% on the whole backward).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       s[b] = f32x16{};
@@ -830,6 +834,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a, MaskDropout md
         dp[b] = mfma32<BF16>(*reinterpret_cast<const s16x8*>(Vs + 32 * b * T::PITCH + ra[t]), oreg[t], dp[b]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       s16x8 sa[2];
