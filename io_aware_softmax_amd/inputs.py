@@ -203,3 +203,23 @@ def additive_mask(seed: int, shape: Sequence[int], sigma: float = 2.0, neg_inf: 
     m[rng.random(tuple(shape)) < neg_inf] = -np.inf
     return m
 
+
+
+def rising_scores(seed: int, B: int, H: int, Lq: int, Lk: int, D: int,
+                  span: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """float32 q, k, v ([B, H, L, D]) whose scores q_i . k_j move steadily
+    along the keys: q_i = a u + e_i and k_j = t_j a u + e'_j with u a random
+    unit vector per (b, h), a = sqrt(span), e, e' of standard deviation 0.1
+    per component, and t_j = j / (Lk - 1) for even heads (scores rising by
+    about ``span`` over a row) or 1 - j / (Lk - 1) for odd heads (the first
+    keys dominate).  v is standard normal.  ``SeedSequence([seed, 8])``."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 8])))
+    u = rng.standard_normal((B, H, 1, D))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    a = math.sqrt(span)
+    t = np.arange(Lk, dtype=np.float64) / max(1, Lk - 1)
+    t = np.where((np.arange(H) % 2 == 0)[None, :, None], t[None, None, :], 1.0 - t[None, None, :])
+    q = a * u + 0.1 * rng.standard_normal((B, H, Lq, D))
+    k = t[..., None] * a * u + 0.1 * rng.standard_normal((B, H, Lk, D))
+    v = rng.standard_normal((B, H, Lk, D))
+    return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)

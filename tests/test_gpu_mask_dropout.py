@@ -198,6 +198,63 @@ def test_ex_deterministic_and_offset_sensitive():
     assert not torch.equal(a, c)
 
 
+# Scores rising by about 60 (base 2) along every row of even heads and
+# falling along odd heads: within a row the kernel's reference value has to
+# move several times (rising), or one early key holds most of the weight
+# (falling: the rounding of the dominant weight).
+REF_MOVES = [  # dtype, D, mask kind, dropout p, Lq, Lk, causal
+    ("bf16", 128, "bool", 0.0, 96, 640, False),
+    ("bf16", 128, "add", 0.0, 320, 320, True),
+    ("bf16", 64, None, 0.3, 96, 640, False),
+    ("bf16", 128, "bool", 0.2, 320, 320, True),
+    ("bf16", 64, "add", 0.0, 96, 640, False),
+    ("f16", 64, "bool", 0.0, 96, 640, False),
+    ("f16", 128, "add", 0.1, 320, 320, True),
+    ("f16", 64, None, 0.3, 320, 320, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,kind,p,Lq,Lk,causal", REF_MOVES)
+def test_ex_reference_moves(dtype, D, kind, p, Lq, Lk, causal):
+    """Forward on ``inputs.rising_scores`` (B1 H2, scale 1/sqrt(D)).
+    Boolean masks (70% kept) also hide keys [0, 150) from 16 rows in the
+    middle of Lq, which then have no visible key for two or more tiles;
+    additive masks are N(0, 15^2) with 10% -inf and every 7th key -1e4.
+
+    Forward only: on rows where one key holds nearly all the weight, the
+    backward's dP - Dv cancels, and Dv = sum_d dO O taken from the stored
+    16-bit O (the output the backward is handed) then moves dQ by several
+    percent of its largest entry, more than the random-input gradient bound
+    allows; the exact-O oracle cannot tell that apart from a kernel error."""
+    import torch
+    from io_aware_softmax_amd import binding
+    B, H = 1, 2
+    scale = 1.0 / np.sqrt(D)
+    seed = 31 * Lq + Lk + D
+    q32, k32, v32 = inputs.rising_scores(seed, B, H, Lq, Lk, D, span=60.0 / (scale * np.log2(np.e)))
+    bits = {t: inputs.round_to(x, dtype) for t, x in zip(("q", "k", "v"), (q32, k32, v32))}
+    q, k, v = (to_device(bits[t], dtype) for t in ("q", "k", "v"))
+    mask = None
+    if kind == "bool":
+        mask = inputs.bool_mask(seed, (B, H, Lq, Lk), keep=0.7)
+        r0 = Lq // 2
+        mask[:, :, r0:r0 + 16, :150] = 0
+    elif kind == "add":
+        mask = inputs.additive_mask(seed, (B, H, Lq, Lk), sigma=15.0, neg_inf=0.1)
+        mask[..., ::7] = -1e4
+    name = f"refmoves_{dtype}_D{D}_{kind}_p{p}_{Lq}x{Lk}_{'causal' if causal else 'full'}"
+    say(f"case {name}")
+    O, L = binding.attn_fwd_ex(q, k, v, causal=causal, scale=scale, mask=_mask_tensor(mask), dropout_p=p, seed=9)
+    torch.cuda.synchronize()
+    vals = {t: inputs.to_float32(bits[t], dtype) for t in ("q", "k", "v")}
+    Or, Lr = oracle.attention_ex(vals["q"], vals["k"], vals["v"], scale, causal, mask=mask, mask_kind=kind,
+                                 dropout_p=p, seed=9)
+    O, L = to_host_f64(O), to_host_f64(L)
+    empty = np.isneginf(Lr)
+    assert np.all(O[empty] == 0) and np.all(np.isneginf(L[empty])), "rows without keys"
+    compare(name, dtype, O[~empty], L[~empty], Or[~empty], Lr[~empty])
+
+
 @pytest.mark.parametrize("B,H,Lq,Lk,D,dtype,causal,kind,mshape,p,scale", [
     (2, 3, 1, 1000, 128, "bf16", False, "bool", "full", 0.25, None),      # one query per (b, h)
     (2, 2, 77, 77, 64, "f16", True, "add", "full", 0.0, -0.3),            # negative scale, full mask
