@@ -260,9 +260,12 @@ def test_ex_reference_moves(dtype, D, kind, p, Lq, Lk, causal):
     (2, 2, 77, 77, 64, "f16", True, "add", "full", 0.0, -0.3),            # negative scale, full mask
     (1, 2, 300, 130, 64, "f16", False, "add", "heads", 0.4, None),        # Lq > Lk
     (3, 2, 65, 129, 128, "bf16", True, "bool", "batch", 0.05, None),      # tile + 1 on both sides
+    (1, 3, 200, 256, 128, "bf16", True, "bool", "shared", 0.0, None),     # odd B*H, one mask for all heads
+    (3, 1, 130, 200, 64, "f16", False, "add", "shared", 0.1, None),       # odd B*H over batches
 ])
 def test_ex_edge_shapes(B, H, Lq, Lk, D, dtype, causal, kind, mshape, p, scale):
-    shape = {"full": (B, H, Lq, Lk), "heads": (1, H, Lq, Lk), "batch": (B, 1, Lq, Lk)}[mshape]
+    shape = {"full": (B, H, Lq, Lk), "heads": (1, H, Lq, Lk), "batch": (B, 1, Lq, Lk),
+             "shared": (1, 1, Lq, Lk)}[mshape]
     if kind == "bool":
         mask = inputs.bool_mask(Lq + Lk, shape, keep=0.7, empty_rows=1)
     else:
