@@ -306,7 +306,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_ex_kernel(PrefillArgs a, MaskDr
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(s[b][8 * half + e]);
-          psum += p;
+          psum = grp || e ? psum + p : p;  // the first weight starts the sum
           const float w = !DROP || ((keep[grp] >> e) & 1u) ? p : 0.f;
           if constexpr (BF16) wmax = fmaxf(wmax, w);
           pb[grp][e] = (short)round16<BF16>(w);

@@ -135,7 +135,7 @@ __device__ __forceinline__ void move_reference(const f32x16 (&s)[2], s16x8 (&pb)
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_use));
       if constexpr (MASK) p = ((live >> (16 * blk + r)) & 1u) ? p : 0.f;
       pb[st][e] = (short)round16<BF16>(p);
-      psum += p;
+      psum = st || e ? psum + p : p;  // the first weight starts the sum
     }
 }
 
@@ -187,7 +187,7 @@ __device__ __forceinline__ void fast_step(const char* kp, const char* vp, const 
     const int blk = e >> 4, r = e & 15;
     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
     pb[e >> 3][e & 7] = (short)round16<BF16>(p);
-    psum += p;
+    psum = e ? psum + p : p;  // the first weight starts the sum
   };
   auto dma = [&](int q) {
     if (q < KP::RUNS) {
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_mfma_kernel(
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -m_use));
         if constexpr (MASK) p = ((live >> (16 * blk + r)) & 1u) ? p : 0.f;
         pb[st][e] = (short)round16<BF16>(p);
-        psum += p;
+        psum = st || e ? psum + p : p;  // the first weight starts the sum
       }
     }
     if constexpr (!BF16) {

@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_pp_kernel(
       const int st = e >> 3, blk = st >> 1, r = 8 * (st & 1) + (e & 7);
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[blk][r], c, neg_m));
       pb[st][e & 7] = (short)round16<BF16>(p);
-      psum += p;
+      psum = e ? psum + p : p;  // the first weight starts the sum (no add of 0)
       if constexpr (BF16) mx = fmaxf(mx, p);
     }
     wmax = mx;
